@@ -1,0 +1,240 @@
+"""Benchmark of the UE5M3-FP4 hot path on one MI355X.
+
+One step = the whole data-parallel hot path of an FFN pair's training step at
+8192 tokens (hidden 4096, FFN 16384): for the up and the down projection,
+quantize X and W (round-to-nearest) and dY (stochastic rounding) in both
+orientations with the tensor-amax by-product, run fprop / dgrad / wgrad
+(six 8192 x 4096 x 16384 block-scaled GEMMs in all), then refresh the six
+tensor scales.  Inputs are seeded synthetic bf16 tensors resident in HBM
+before timing starts.
+
+Prints one JSON line.  `value` is the step's GEMM work (6 x 1.0995e12 flop)
+divided by the measured step time, in TFLOP/s.  `roofline` is for the GEMM
+kernel (the dominant kernel): algorithmic flops per launch over its average
+launch time, measured with HIP events on the stream it runs on, against the
+bf16 dense MFMA peak (the kernel feeds exact bf16 dequantizations to bf16
+MFMA).  `quantize` reports the quantizer's GB/s against HBM peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "UE5M3-FP4 GEMM TFLOP/s (fprop/dgrad/wgrad) + quantize GB/s, % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+TOKENS, HIDDEN, FFN = 8192, 4096, 16384
+QUANT_BYTES_PER_ELEM = 2.0 + 2 * 0.5625  # bf16 in; codes + scales out, both orientations
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--period", type=int, default=1, help="tensor-scale refresh period")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Tensor:
+    """One bf16 operand of the step with its quantized buffers and scale state."""
+
+    def __init__(self, lib, torch, bits, rounding, tid):
+        self.x = torch.from_numpy(bits.view("int16")).cuda()
+        rows, cols = bits.shape
+        self.ts = torch.ones(1, dtype=torch.float32, device="cuda")
+        self.amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.row = lib.empty_quantized(rows, cols, self.ts)
+        self.col = lib.empty_quantized(cols, rows, self.ts)
+        self.rounding = rounding
+        self.tid = tid
+        self.elems = rows * cols
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_block_scaled_amax_amd as lib
+    from workloads import config, sr_seed
+
+    lib.load_library()
+    torch.cuda.set_device(0)
+    data = config(4)
+    seed = sr_seed(4)
+    layers = []
+    tid = 0
+    for xn, wn, dn in (("X", "W_up", "dY_up"), ("H", "W_down", "dY_down")):
+        X = Tensor(lib, torch, data[xn], lib.RNE, tid)
+        W = Tensor(lib, torch, data[wn], lib.RNE, tid + 1)
+        D = Tensor(lib, torch, data[dn], lib.SR, tid + 2)
+        tid += 3
+        tokens, in_f = data[xn].shape
+        out_f = data[wn].shape[0]
+        Y = torch.empty((tokens, out_f), dtype=torch.float32, device="cuda")
+        dX = torch.empty((tokens, in_f), dtype=torch.float32, device="cuda")
+        dW = torch.empty((out_f, in_f), dtype=torch.float32, device="cuda")
+        layers.append((X, W, D, Y, dX, dW, tokens, in_f, out_f))
+    del data
+    tensors = [t for L in layers for t in L[:3]]
+    n_tensors = len(tensors)
+    gemm_flops = [2.0 * L[6] * L[7] * L[8] for L in layers for _ in range(3)]
+    step_flops = float(sum(gemm_flops))
+    quant_bytes = sum(t.elems for t in tensors) * QUANT_BYTES_PER_ELEM
+
+    # bootstrap: amax-only pass, then the first refresh (step 0)
+    for t in tensors:
+        lib.quantize_blockscale(t.x, None, amax=t.amax)
+        lib.update_tensor_scale(t.amax, t.ts, 0, 1)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(s, timing=None):
+        for L in layers:
+            X, W, D, Y, dX, dW = L[:6]
+            for t in (X, W, D):
+                e0 = ev() if timing is not None else None
+                if e0:
+                    e0.record()
+                lib.quantize_blockscale(t.x, t.ts, t.rounding, seed, s * n_tensors + t.tid,
+                                        row=t.row, col=t.col, amax=t.amax)
+                if e0:
+                    e1 = ev()
+                    e1.record()
+                    timing["quantize"].append((e0, e1, t.elems))
+            for fn, a, b, c in ((lib.gemm_fprop, X.row, W.row, Y), (lib.gemm_dgrad, D.row, W.col, dX),
+                                (lib.gemm_wgrad, D.col, X.col, dW)):
+                e0 = ev() if timing is not None else None
+                if e0:
+                    e0.record()
+                fn(a, b, c)
+                if e0:
+                    e1 = ev()
+                    e1.record()
+                    timing["gemm"].append((e0, e1, 2.0 * c.shape[0] * c.shape[1] * a.cols))
+        for t in tensors:
+            lib.update_tensor_scale(t.amax, t.ts, s + 1, args.period)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, wall clock and stream events
+    timing = {"quantize": [], "gemm": []}
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s, timing)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    wall_ms = wall * 1e3 / args.steps
+
+    gemm_ms = [a.elapsed_time(b) for a, b, _ in timing["gemm"]]
+    gemm_fl = [f for _, _, f in timing["gemm"]]
+    q_ms = [a.elapsed_time(b) for a, b, _ in timing["quantize"]]
+    q_el = [n for _, _, n in timing["quantize"]]
+    gemm_avg_ms = float(np.mean(gemm_ms))
+    gemm_tflops = float(np.sum(gemm_fl) / (np.sum(gemm_ms) * 1e-3) / 1e12)
+    q_gbs = float(np.sum(q_el) * QUANT_BYTES_PER_ELEM / (np.sum(q_ms) * 1e-3) / 1e9)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ffn_pair_fwd_bwd", "tokens": TOKENS, "hidden": HIDDEN,
+                   "ffn": FFN, "gemms_per_step": 6, "quantize_calls_per_step": 6,
+                   "tensor_scale_period": args.period,
+                   "gemm_shape": "8192x4096x16384 (M,N,K permuted)",
+                   "formats": "E2M1 payload, UE5M3 block-16 scales, fp32 tensor scale; "
+                              "GEMM: exact bf16 dequant -> bf16 MFMA, fp32 accumulate"},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel",
+                     "achieved": round(gemm_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "avg_launch_ms": round(gemm_avg_ms, 4),
+                     "flop_per_launch": gemm_fl[0], "traffic": None},
+        "quantize": {"achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                     "avg_launch_ms": round(float(np.mean(q_ms)), 4),
+                     "bytes_per_elem": QUANT_BYTES_PER_ELEM},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(step_flops, sum(t.elems for t in tensors))
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(step_flops, step_elems):
+    """The CPU oracle (as it stands) on a bounded sample of one step: the
+    quantization of 64 output rows of dY_up in both orientations (SR) and
+    the fp64 GEMM of 16 output rows of the up projection's fprop.  The step
+    time is extrapolated per element and per flop, and reported in the same
+    TFLOP/s unit as `value`."""
+    import numpy as np
+
+    from oracle import gemm, quantize
+    from workloads import config, sr_seed
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    data = config(4)
+    dy = data["dY_up"]
+    t0 = time.perf_counter()
+    q_rows = 64
+    for o, n_out in ((0, dy.shape[0]), (1, dy.shape[1])):
+        rows = np.arange(q_rows) * (n_out // q_rows)
+        quantize.quantize_blockscale(dy, np.float32(1e-7), quantize.SR, sr_seed(4), 0, o, rows=rows)
+    tq = time.perf_counter() - t0
+    q_elems = 2 * q_rows * dy.shape[1]  # output elements produced (avg over orientations)
+    x = data["X"][:16]
+    w = data["W_up"]
+    xc, xs = quantize.quantize_blockscale(x, np.float32(1e-4), quantize.RNE)
+    wc, ws = quantize.quantize_blockscale(w, np.float32(1e-6), quantize.RNE)
+    t1 = time.perf_counter()
+    gemm.gemm_nt(xc, xs, 1e-4, wc, ws, 1e-6)
+    tg = time.perf_counter() - t1
+    g_flops = 2.0 * 16 * w.shape[0] * w.shape[1]
+    # every input element is quantized in two orientations per step
+    est_step_s = tq / q_elems * (2 * step_elems) + tg / g_flops * step_flops
+    return {"value": round(step_flops / est_step_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"quantize (SR) of {q_rows} output rows per orientation of dY_up "
+                      f"8192x16384 ({tq:.1f} s) + fp64 fprop GEMM of 16 x 16384 x 4096 "
+                      f"({tg:.1f} s, dequantize included); step time extrapolated per element "
+                      f"and per flop: {est_step_s:.0f} s"}
+
+
+if __name__ == "__main__":
+    main()

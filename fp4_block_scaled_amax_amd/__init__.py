@@ -1,0 +1,250 @@
+"""Python binding of libue5m3fp4: UE5M3-FP4 block-16 quantization and the
+block-scaled training GEMMs on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libue5m3fp4.so (built in-tree by fp4_block_scaled_amax_amd/build.py).  The
+functions take torch tensors for device memory and use torch's current HIP
+stream unless one is given.  There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+
+The method: "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining"
+(arXiv 2609.02846), abstract.  The C ABI and all layouts are documented in
+include/ue5m3fp4.h.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libue5m3fp4.so")
+
+RNE = 0
+SR = 1
+MAX_SAFE_DEFAULT = 7168.0  # 114688 / 16: block scale of the largest block at refresh time
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "ue5m3fp4_quantize_blockscale": [_c_void_p, _i64, _i64, _i64, _c_void_p, ctypes.c_int,
+                                     ctypes.c_uint64, ctypes.c_uint32, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "ue5m3fp4_dequantize": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_nt": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_fprop": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_dgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_wgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_update_tensor_scale": [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_float,
+                                     _c_void_p],
+}
+
+_lib = None
+
+
+class Ue5m3Fp4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def load_library(path=LIB_PATH):
+    """Load libue5m3fp4.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m fp4_block_scaled_amax_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ue5m3fp4_status_string.argtypes = [ctypes.c_int]
+    lib.ue5m3fp4_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().ue5m3fp4_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise Ue5m3Fp4Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _require(t, dtypes, name, dims=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions")
+
+
+@dataclass
+class Quantized:
+    """One block-scaled operand: codes [R][C/2] uint8, scales [R][C/16] uint8,
+    ts = device fp32 tensor scale (1 element).  Blocks run along C."""
+
+    codes: "object"
+    scales: "object"
+    ts: "object"
+
+    @property
+    def rows(self):
+        return self.codes.shape[0]
+
+    @property
+    def cols(self):
+        return self.codes.shape[1] * 2
+
+
+def empty_quantized(rows, cols, ts, device=None):
+    """Allocate the code and scale buffers of a rows x cols operand."""
+    import torch
+
+    device = device if device is not None else ts.device
+    return Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                     torch.empty((rows, cols // 16), dtype=torch.uint8, device=device), ts)
+
+
+def quantize_blockscale(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=None, col=None,
+                        amax=None, stream=None):
+    """Quantize a bf16 (rows x cols) tensor.  row / col: Quantized outputs (or
+    (codes, scales) pairs) for the row-wise and the transposed orientation, or
+    None.  amax: device fp32 scalar that receives max(amax, max|x|)."""
+    import torch
+
+    _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its columns")
+    rc = rs = cc = cs = None
+    if row is not None:
+        rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
+    if col is not None:
+        cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
+    for t, n in ((rc, "row codes"), (rs, "row scales"), (cc, "col codes"), (cs, "col scales")):
+        if t is not None:
+            _require(t, (torch.uint8,), n)
+    if tensor_scale is not None:
+        _require(tensor_scale, (torch.float32,), "tensor_scale")
+    if amax is not None:
+        _require(amax, (torch.float32,), "amax")
+    rows, cols = x.shape
+    if rc is not None and (tuple(rc.shape) != (rows, cols // 2) or tuple(rs.shape) != (rows, cols // 16)):
+        raise ValueError("row output buffers have the wrong shape")
+    if cc is not None and (tuple(cc.shape) != (cols, rows // 2) or tuple(cs.shape) != (cols, rows // 16)):
+        raise ValueError("col output buffers have the wrong shape")
+    st = load_library().ue5m3fp4_quantize_blockscale(
+        _ptr(x), rows, cols, x.stride(0), _ptr(tensor_scale), int(rounding), int(seed),
+        int(offset), _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs), _ptr(amax), _stream(stream))
+    _check(st, "ue5m3fp4_quantize_blockscale")
+
+
+def dequantize(q, out, stream=None):
+    """out (fp32 [R][C]) = ts * s_b * e2m1 of the quantized operand q."""
+    import torch
+
+    _require(out, (torch.float32,), "out", 2)
+    if tuple(out.shape) != (q.rows, q.cols):
+        raise ValueError("out has the wrong shape")
+    st = load_library().ue5m3fp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.ts), q.rows,
+                                            q.cols, _ptr(out), _stream(stream))
+    _check(st, "ue5m3fp4_dequantize")
+    return out
+
+
+def _gemm_out(out, m, n):
+    import torch
+
+    _require(out, (torch.float32,), "out", 2)
+    if tuple(out.shape) != (m, n) or not out.is_contiguous():
+        raise ValueError(f"output must be a contiguous fp32 [{m}][{n}] tensor")
+
+
+def gemm_nt(a, b, out, stream=None):
+    """out[M][N] = tsA * tsB * A B^T with A (M x K) and B (N x K) blocked along K."""
+    if a.cols != b.cols:
+        raise ValueError("A and B disagree on K")
+    _gemm_out(out, a.rows, b.rows)
+    st = load_library().ue5m3fp4_gemm_nt(_ptr(a.codes), _ptr(a.scales), _ptr(a.ts),
+                                         _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
+                                         b.rows, a.cols, _ptr(out), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_nt")
+    return out
+
+
+def gemm_fprop(x_row, w_row, y, stream=None):
+    """Y [tokens][out] = X W^T from X and W quantized row-wise."""
+    tokens, in_f = x_row.rows, x_row.cols
+    out_f = w_row.rows
+    if w_row.cols != in_f:
+        raise ValueError("X and W disagree on in_features")
+    _gemm_out(y, tokens, out_f)
+    st = load_library().ue5m3fp4_gemm_fprop(_ptr(x_row.codes), _ptr(x_row.scales), _ptr(x_row.ts),
+                                            _ptr(w_row.codes), _ptr(w_row.scales), _ptr(w_row.ts),
+                                            tokens, in_f, out_f, _ptr(y), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_fprop")
+    return y
+
+
+def gemm_dgrad(dy_row, w_col, dx, stream=None):
+    """dX [tokens][in] = dY W from dY row-wise and W's transposed output."""
+    tokens, out_f = dy_row.rows, dy_row.cols
+    in_f = w_col.rows
+    if w_col.cols != out_f:
+        raise ValueError("dY and W^T disagree on out_features")
+    _gemm_out(dx, tokens, in_f)
+    st = load_library().ue5m3fp4_gemm_dgrad(_ptr(dy_row.codes), _ptr(dy_row.scales),
+                                            _ptr(dy_row.ts), _ptr(w_col.codes),
+                                            _ptr(w_col.scales), _ptr(w_col.ts), tokens, in_f,
+                                            out_f, _ptr(dx), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_dgrad")
+    return dx
+
+
+def gemm_wgrad(dy_col, x_col, dw, stream=None):
+    """dW [out][in] = dY^T X from the transposed outputs of dY and X."""
+    out_f, tokens = dy_col.rows, dy_col.cols
+    in_f = x_col.rows
+    if x_col.cols != tokens:
+        raise ValueError("dY^T and X^T disagree on tokens")
+    _gemm_out(dw, out_f, in_f)
+    st = load_library().ue5m3fp4_gemm_wgrad(_ptr(dy_col.codes), _ptr(dy_col.scales),
+                                            _ptr(dy_col.ts), _ptr(x_col.codes),
+                                            _ptr(x_col.scales), _ptr(x_col.ts), tokens, in_f,
+                                            out_f, _ptr(dw), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_wgrad")
+    return dw
+
+
+def update_tensor_scale(amax_running, tensor_scale, step, period=1,
+                        max_safe=MAX_SAFE_DEFAULT, stream=None):
+    """Periodic refresh: at step % period == 0, ts = amax / (6 max_safe) if
+    amax is finite and > 0, and amax is reset to 0 (both device scalars)."""
+    import torch
+
+    _require(amax_running, (torch.float32,), "amax_running")
+    _require(tensor_scale, (torch.float32,), "tensor_scale")
+    st = load_library().ue5m3fp4_update_tensor_scale(_ptr(amax_running), _ptr(tensor_scale),
+                                                     int(step), int(period), float(max_safe),
+                                                     _stream(stream))
+    _check(st, "ue5m3fp4_update_tensor_scale")

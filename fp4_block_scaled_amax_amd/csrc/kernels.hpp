@@ -1,0 +1,45 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Callers have validated every argument; launchers only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ue5m3fp4 {
+
+struct QuantizeArgs {
+    const uint16_t* x;
+    int64_t rows, cols, ld;
+    const float* tensor_scale;
+    bool stochastic;
+    uint64_t seed;
+    uint32_t offset;
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    uint8_t* col_codes;
+    uint8_t* col_scales;
+    float* amax_inout;
+};
+
+void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t stream);
+
+void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                       int64_t rows, int64_t cols, float* out, hipStream_t stream);
+
+void launch_update_tensor_scale(float* amax_running, float* tensor_scale, float max_safe,
+                                hipStream_t stream);
+
+struct GemmArgs {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const float* a_ts;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* b_ts;
+    int64_t M, N, K;
+    float* c;
+};
+
+void launch_gemm_nt(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace ue5m3fp4

@@ -1,0 +1,84 @@
+"""Helpers for the GPU tests: move seeded inputs to the device, run the HIP
+path through the C ABI (via the binding), and compare with the oracle."""
+
+import numpy as np
+
+import fp4_block_scaled_amax_amd as lib
+from oracle import formats, gemm, quantize, tensor_scale
+
+
+def dev_bf16(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def dev_scalar(v):
+    import torch
+
+    return torch.tensor([np.float32(v)], dtype=torch.float32, device="cuda")
+
+
+def fresh_ts(bits):
+    """Tensor scale refreshed from this tensor's own amax (oracle arithmetic)."""
+    _, ts = tensor_scale.update_tensor_scale(quantize.tensor_amax(bits), np.float32(1.0), 0, 1)
+    return ts
+
+
+def gpu_quantize(x_dev, ts, rounding=lib.RNE, seed=0, offset=0, row=True, col=True, amax=None):
+    """Returns (row Quantized or None, col Quantized or None)."""
+    rows, cols = x_dev.shape
+    ts_dev = ts if hasattr(ts, "is_cuda") else dev_scalar(ts)
+    qr = lib.empty_quantized(rows, cols, ts_dev) if row else None
+    qc = lib.empty_quantized(cols, rows, ts_dev) if col else None
+    lib.quantize_blockscale(x_dev, ts_dev, rounding, seed, offset, row=qr, col=qc, amax=amax)
+    return qr, qc
+
+
+def host(t):
+    import torch
+
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_quant_equal(q_dev, bits, ts, rounding, seed, offset, orientation, rows=None):
+    """Bit-exact comparison of codes and scales with the oracle, on all output
+    rows or on the sampled output rows `rows`."""
+    codes = host(q_dev.codes)
+    scales = host(q_dev.scales)
+    oc, os_ = quantize.quantize_blockscale(bits, ts, rounding, seed, offset, orientation, rows=rows)
+    if rows is not None:
+        codes, scales = codes[rows], scales[rows]
+    bad_s = np.argwhere(scales != os_)
+    assert bad_s.size == 0, f"scale mismatch at {bad_s[:5].tolist()}: gpu {scales[tuple(bad_s[0])]:#x} oracle {os_[tuple(bad_s[0])]:#x}"
+    bad_c = np.argwhere(codes != oc)
+    assert bad_c.size == 0, f"code mismatch at {bad_c[:5].tolist()}: gpu {codes[tuple(bad_c[0])]:#x} oracle {oc[tuple(bad_c[0])]:#x}"
+
+
+def assert_gemm_close(c_gpu, a_codes, a_scales, ts_a, b_codes, b_scales, ts_b, rows=None, cols=None,
+                      rtol=1e-5):
+    """|C_gpu - C_ref| <= rtol * |tsA tsB| * sum|a||b| per element, on all
+    elements or on the sampled (rows[t], cols[t]) entries.  NaN must match."""
+    if rows is None:
+        ref, bound = gemm.gemm_nt(a_codes, a_scales, ts_a, b_codes, b_scales, ts_b)
+        got = c_gpu.astype(np.float64)
+    else:
+        ref, bound = gemm.gemm_nt_entries(a_codes, a_scales, ts_a, b_codes, b_scales, ts_b,
+                                          rows, cols)
+        got = c_gpu[rows, cols].astype(np.float64)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "NaN pattern differs"
+    err = np.abs(got - ref)[~nan_ref]
+    lim = (rtol * bound)[~nan_ref]
+    worst = np.argmax(err - lim) if err.size else 0
+    assert np.all(err <= lim), (f"gemm error {err.flat[worst]:.3e} > {lim.flat[worst]:.3e} "
+                                f"(ref {ref[~nan_ref].flat[worst]:.6e})")
+    return float(np.max(err / np.maximum(bound[~nan_ref], 1e-300))) if err.size else 0.0
+
+
+def sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(n, size=min(k, n), replace=False)
+    pick[:2] = [0, n - 1] if n > 1 else [0, 0]
+    return np.unique(pick)

@@ -1,0 +1,178 @@
+"""GPU parity of the block-scaled GEMMs (HIP kernel through the C ABI).
+
+C = tsA * tsB * A B^T with fp32 accumulation; several results are correct
+(the accumulation order is free), so each element must satisfy
+|C_gpu - C_oracle| <= 1e-5 * |tsA tsB| * sum_k |a_k b_k|.  Operands come from
+the GPU quantizer, whose codes are bit-exact with the oracle (tested
+separately); the oracle GEMM consumes the same code bytes.  "Rethinking
+Shrinkage Bias in LLM FP4 Pretraining ... UFP4 Recipe", abstract: the three
+training GEMMs; "UE5M3 FP4 Block Scaling for Stable Language Model
+Pretraining", abstract: UE5M3 block-16 operands.
+"""
+
+import numpy as np
+import pytest
+
+import fp4_block_scaled_amax_amd as lib
+from oracle import formats, quantize
+from workloads import config, random_bf16, sr_seed, STALE_FACTORS
+
+from devhelpers import (assert_gemm_close, assert_quant_equal, dev_bf16, dev_scalar, fresh_ts,
+                        gpu_quantize, host, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _empty(m, n):
+    import torch
+
+    return torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _random_operand(rng, rows, k, lo=0x40, hi=0xB0, ts=1.0):
+    import torch
+
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(lo, hi, size=(rows, k // 16), dtype=np.uint8)
+    q = lib.Quantized(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                      dev_scalar(ts))
+    return q, codes, scales
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (300, 200, 4112),
+                                   (1, 1, 16), (33, 130, 48), (129, 257, 144), (64, 64, 2048)])
+def test_gemm_nt_random_codes_full(cuda_device, M, N, K):
+    """Random code bytes and scales (including subnormal scales): whole
+    output compared, multiple tiles, ragged M, N and K tails."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a, ac, asc = _random_operand(rng, M, K, 0x01, 0xFF, ts=0.75)
+    b, bc, bsc = _random_operand(rng, N, K, 0x01, 0xFF, ts=1.5e-3)
+    c = _empty(M, N)
+    lib.gemm_nt(a, b, c)
+    assert_gemm_close(host(c), ac, asc, 0.75, bc, bsc, 1.5e-3)
+
+
+def test_gemm_k_zero_writes_zeros(cuda_device):
+    import torch
+
+    a = lib.Quantized(torch.zeros((4, 0), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((4, 0), dtype=torch.uint8, device="cuda"), dev_scalar(1.0))
+    b = lib.Quantized(torch.zeros((3, 0), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((3, 0), dtype=torch.uint8, device="cuda"), dev_scalar(1.0))
+    c = _empty(4, 3)
+    lib.gemm_nt(a, b, c)
+    assert np.all(host(c) == 0)
+
+
+def test_gemm_nan_scale_row(cuda_device):
+    rng = np.random.default_rng(5)
+    a, ac, asc = _random_operand(rng, 64, 64)
+    b, bc, bsc = _random_operand(rng, 48, 64)
+    a.scales[7, 2] = 0xFF
+    asc[7, 2] = 0xFF
+    c = _empty(64, 48)
+    lib.gemm_nt(a, b, c)
+    got = host(c)
+    assert np.all(np.isnan(got[7])) and np.isfinite(np.delete(got, 7, axis=0)).all()
+    assert_gemm_close(got, ac, asc, 1.0, bc, bsc, 1.0)
+
+
+def _linear_layer(X, W, dY, seed, offset0=0, ts=None, rows_sample=None):
+    """Quantize X, W (RNE) and dY (SR) in both orientations on the GPU, check
+    the codes against the oracle, run fprop / dgrad / wgrad and check them."""
+    ts = ts or {}
+    tsX = ts.get("X", fresh_ts(X))
+    tsW = ts.get("W", fresh_ts(W))
+    tsD = ts.get("dY", fresh_ts(dY))
+    xr, xc = gpu_quantize(dev_bf16(X), tsX, lib.RNE)
+    wr, wc = gpu_quantize(dev_bf16(W), tsW, lib.RNE)
+    dr, dc = gpu_quantize(dev_bf16(dY), tsD, lib.SR, seed=seed, offset=offset0)
+    tokens, in_f = X.shape
+    out_f = W.shape[0]
+    y, dx, dw = _empty(tokens, out_f), _empty(tokens, in_f), _empty(out_f, in_f)
+    lib.gemm_fprop(xr, wr, y)
+    lib.gemm_dgrad(dr, wc, dx)
+    lib.gemm_wgrad(dc, xc, dw)
+    worst = 0.0
+    for c, (qa, ta), (qb, tb) in ((y, (xr, tsX), (wr, tsW)), (dx, (dr, tsD), (wc, tsW)),
+                                  (dw, (dc, tsD), (xc, tsX))):
+        got = host(c)
+        m, n = got.shape
+        if rows_sample:
+            rng = np.random.default_rng(m + n)
+            rr = rng.integers(0, m, rows_sample)
+            cc = rng.integers(0, n, rows_sample)
+            rr[:2], cc[:2] = [0, m - 1], [0, n - 1]
+            e = assert_gemm_close(got, host(qa.codes), host(qa.scales), ta, host(qb.codes),
+                                  host(qb.scales), tb, rr, cc)
+        else:
+            e = assert_gemm_close(got, host(qa.codes), host(qa.scales), ta, host(qb.codes),
+                                  host(qb.scales), tb)
+        worst = max(worst, e)
+    return dict(X=(xr, xc, tsX), W=(wr, wc, tsW), dY=(dr, dc, tsD), worst=worst)
+
+
+def test_config1_roundtrip_and_fprop(cuda_device):
+    """256 x 256 X and W ~ N(0,1), seed 0, fresh tensor scales, RNE: codes,
+    scales and dequantization bit-exact; fprop within tolerance."""
+    import torch
+
+    data = config(1)
+    X, W = data["X"], data["W"]
+    tsX, tsW = fresh_ts(X), fresh_ts(W)
+    xr, _ = gpu_quantize(dev_bf16(X), tsX, lib.RNE, col=False)
+    wr, _ = gpu_quantize(dev_bf16(W), tsW, lib.RNE, col=False)
+    assert_quant_equal(xr, X, tsX, lib.RNE, 0, 0, 0)
+    assert_quant_equal(wr, W, tsW, lib.RNE, 0, 0, 0)
+    for q, ts in ((xr, tsX), (wr, tsW)):
+        out = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+        lib.dequantize(q, out)
+        ref = quantize.dequantize(host(q.codes), host(q.scales), ts)
+        assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+    y = _empty(256, 256)
+    lib.gemm_fprop(xr, wr, y)
+    assert_gemm_close(host(y), host(xr.codes), host(xr.scales), tsX, host(wr.codes),
+                      host(wr.scales), tsW)
+
+
+def test_small_linear_layer_full(cuda_device):
+    X = random_bf16((272, 400), seed=1)
+    W = random_bf16((176, 400), seed=2, kind="heavy")
+    dY = random_bf16((272, 176), seed=3, kind="gradient")
+    r = _linear_layer(X, W, dY, seed=17)
+    for name, bits in (("X", X), ("W", W), ("dY", dY)):
+        qr, qc, ts = r[name]
+        rnd = lib.SR if name == "dY" else lib.RNE
+        assert_quant_equal(qr, bits, ts, rnd, 17 if rnd else 0, 0, 0)
+        assert_quant_equal(qc, bits, ts, rnd, 17 if rnd else 0, 0, 1)
+
+
+def test_config3_attention_projection(cuda_device):
+    """tokens 8192, in 4096, out 4096: fprop / dgrad / wgrad, SR on dY only."""
+    d = config(3)
+    r = _linear_layer(d["X"], d["W"], d["dY"], seed=sr_seed(3), rows_sample=1500)
+    for name in ("X", "W", "dY"):
+        qr, qc, ts = r[name]
+        bits = d[name]
+        rnd = lib.SR if name == "dY" else lib.RNE
+        seed = sr_seed(3) if rnd else 0
+        assert_quant_equal(qr, bits, ts, rnd, seed, 0, 0, rows=sample_rows(bits.shape[0], 24, 5))
+        assert_quant_equal(qc, bits, ts, rnd, seed, 0, 1, rows=sample_rows(bits.shape[1], 24, 6))
+
+
+def test_config4_ffn_pair(cuda_device):
+    """FFN up (4096 -> 16384) and down (16384 -> 4096) layers at 8192 tokens:
+    six GEMMs, each 8192 x 4096 x 16384 in some order, on sampled entries."""
+    d = config(4)
+    _linear_layer(d["X"], d["W_up"], d["dY_up"], seed=sr_seed(4), offset0=0, rows_sample=600)
+    _linear_layer(d["H"], d["W_down"], d["dY_down"], seed=sr_seed(4), offset0=1, rows_sample=600)
+
+
+@pytest.mark.parametrize("factor", STALE_FACTORS)
+def test_config5_gemms_with_stale_scales(cuda_device, factor):
+    d = config(5)
+    ts = {}
+    for name in ("X", "W", "dY"):
+        a = quantize.tensor_amax(d[name]) * np.float32(factor)
+        ts[name] = np.float32(a / np.float32(43008.0))
+    _linear_layer(d["X"], d["W"], d["dY"], seed=sr_seed(5), ts=ts, rows_sample=1500)
