@@ -176,3 +176,36 @@ def test_config5_gemms_with_stale_scales(cuda_device, factor):
         a = quantize.tensor_amax(d[name]) * np.float32(factor)
         ts[name] = np.float32(a / np.float32(43008.0))
     _linear_layer(d["X"], d["W"], d["dY"], seed=sr_seed(5), ts=ts, rows_sample=1500)
+
+
+def test_dequant_exhaustive_through_gemm(cuda_device):
+    """Every (E2M1 code, UE5M3 scale) pair, exactly: row i of A holds pair i at
+    k = 0 (zeros elsewhere), B has a single 1.0 (code 2, scale 0x78) at k = 0,
+    so C[i][0] = q * s must come out exact.  Repeated at every position of a
+    128-element K chunk to cover every lane and nibble of the fragment layout."""
+    import torch
+
+    codes_q = np.arange(16)
+    codes_s = np.arange(256)
+    pairs = np.array([(c, s) for s in codes_s for c in codes_q])  # 4096 pairs
+    M, K = len(pairs), 128
+    for pos in (0, 1, 7, 8, 15, 16, 33, 64, 100, 127):
+        ac = np.zeros((M, K // 2), np.uint8)
+        asc = np.full((M, K // 16), 0x78, np.uint8)
+        byte = pos // 2
+        ac[:, byte] = (pairs[:, 0] << (4 * (pos % 2))).astype(np.uint8)
+        asc[:, pos // 16] = pairs[:, 1]
+        bc = np.zeros((16, K // 2), np.uint8)
+        bsc = np.full((16, K // 16), 0x78, np.uint8)
+        bc[0, byte] = 2 << (4 * (pos % 2))  # 1.0
+        a = lib.Quantized(torch.from_numpy(ac).cuda(), torch.from_numpy(asc).cuda(), dev_scalar(1.0))
+        b = lib.Quantized(torch.from_numpy(bc).cuda(), torch.from_numpy(bsc).cuda(), dev_scalar(1.0))
+        c = _empty(M, 16)
+        lib.gemm_nt(a, b, c)
+        got = host(c)[:, 0].astype(np.float64)
+        ref = formats.e2m1_decode(pairs[:, 0]) * formats.ue5m3_decode(pairs[:, 1])
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), pos
+        assert np.array_equal(got[~nan], ref[~nan]), (pos, np.argwhere(got[~nan] != ref[~nan])[:4])
+        rest = host(c)[:, 1:]  # B rows of zeros: 0, or NaN where A's block scale is NaN
+        assert np.all(rest[~nan] == 0) and np.all(np.isnan(rest[nan]))
