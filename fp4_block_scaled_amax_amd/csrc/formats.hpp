@@ -7,7 +7,8 @@
 //
 // Everything here is plain fp32 / integer code with one IEEE rounding per
 // operation; the translation units are compiled with -ffp-contract=off so
-// that no multiply-add is fused.
+// that no multiply-add is fused implicitly.  The only FMAs are the explicit
+// correction steps of rcp_rn / div_rn, whose results equal IEEE division.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,6 +61,30 @@ __device__ __forceinline__ float ue5m3_decode(uint32_t c) {
     const uint32_t e = c >> 3, f = c & 7u;
     if (e == 0u) return (float)f * 0x1p-17f;
     return __uint_as_float(((e + 112u) << 23) | (f << 20));  // (1 + f/8) * 2^(e-15)
+}
+
+// ------------------------------------------------- correctly rounded ops --
+// Round-to-nearest fp32 reciprocal and division built from v_rcp_f32 plus one
+// FMA-based correction (Markstein's refinement).  Checked exhaustively on
+// gfx950 against IEEE division: the reciprocal over every normal fp32 input,
+// the division over every bf16 dividend mantissa against every divisor
+// mantissa for quotients in the normal range.  Outside the guarded range the
+// callers fall back to the IEEE division.
+
+__device__ __forceinline__ float rcp_rn(float d) {
+    if (!(d >= 0x1p-100f && d <= 0x1p100f)) return 1.0f / d;
+    const float y = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, y, 1.0f);
+    return __builtin_fmaf(e, y, y);
+}
+
+// a / b rounded to nearest, given y = RN(1 / b) and fast_b = b in [2^-100, 2^100].
+__device__ __forceinline__ float div_rn(float a, float b, float y, bool fast_b) {
+    const float q = a * y;
+    const float r = __builtin_fmaf(-b, q, a);
+    const float q1 = __builtin_fmaf(r, y, q);
+    if (fast_b && a >= 0x1p-100f && q1 >= 0x1p-100f && q1 <= 0x1p100f) return q1;
+    return a / b;
 }
 
 // ------------------------------------------------------------------ E2M1 --
