@@ -102,24 +102,21 @@ __device__ __forceinline__ uint32_t e2m1_rne_index(float a) {
 
 // Stochastic-rounding magnitude index of a = |v| with 16 random bits u:
 // with lo the grid value below a and step the gap to the next one, round up
-// iff u < 65536 * (a - lo) / step.  The differences are exact (Sterbenz) and
-// the scalings are powers of two, so the comparison is exact.  a >= 6 gives
-// 7; NaN gives 0.
+// iff u < 65536 * (a - lo) / step.  Branch-free: within each stretch of the
+// grid with one step (0..2 step 0.5, 2..4 step 1, 4..6 step 2) a is scaled by
+// 1/step (a power of two, exact), so the integer part gives lo's index (plus
+// 0, 2 or 4) and the fraction (exact by Sterbenz) is (a - lo) / step.  a >= 6
+// gives 7; NaN gives 0.
 __device__ __forceinline__ uint32_t e2m1_sr_index(float a, uint32_t u) {
-    const float uf = (float)u;
-    if (a < 2.0f) {  // grid 0, .5, 1, 1.5 (indices 0..3), step 0.5
-        const float t = a * 2.0f;
-        const float lo = truncf(t);
-        return (uint32_t)lo + (uint32_t)(uf < (t - lo) * 65536.0f);
-    }
-    if (a < 4.0f) {  // grid 2, 3 (indices 4, 5), step 1
-        const float lo = truncf(a);
-        return (uint32_t)lo + 2u + (uint32_t)(uf < (a - lo) * 65536.0f);
-    }
-    if (a < 6.0f) {  // grid 4 (index 6), step 2
-        return 6u + (uint32_t)(uf < ((a - 4.0f) * 0.5f) * 65536.0f);
-    }
-    return a >= 6.0f ? 7u : 0u;  // saturate; NaN -> 0
+    const bool r1 = a < 2.0f, r2 = a < 4.0f;
+    const float scale = r1 ? 2.0f : (r2 ? 1.0f : 0.5f);
+    const uint32_t add = r1 ? 0u : (r2 ? 2u : 4u);
+    const float t = fminf(a, 7.0f) * scale;  // in [0, 4): exact
+    const float fl = truncf(t);
+    const float frac = t - fl;
+    const uint32_t up = (float)u < frac * 65536.0f;
+    const uint32_t idx = (uint32_t)fl + add + up;
+    return a >= 6.0f ? 7u : (a == a ? idx : 0u);
 }
 
 // ---------------------------------------------------------------- Philox --
