@@ -22,24 +22,30 @@
 //                                         exponent of its fp32 scale operand)
 //   v_pk_mul_f16               * m       (m = 8 + f for a normal UE5M3 code
 //                                         (e, f), f for a subnormal one)
-// with E = max(e, 1) - 22, so q * 2^E * m = q * s / 16.  A 256-entry table in
-// LDS holds (2^E as fp32, m as packed fp16) for every scale byte; 0xFF maps
-// to m = NaN so a NaN block poisons its output as the format requires.
+// with E = max(e, 1) - 22, so q * 2^E * m = q * s / 16.  Both factors live in
+// one "expanded scale" dword: its fp32 exponent field carries E, its low
+// half carries m as fp16 (the multiply broadcasts the low half).  A 256-entry
+// table maps each scale byte to its dword; 0xFF maps to m = NaN so a NaN
+// block poisons its outputs as the format requires.
 //
 // Tiling.  256 x 256 workgroup tile, 4 waves of 128 x 128 (4 x 4 MFMA tiles,
 // 256 fp32 accumulators per lane), K chunks of 128 elements double-buffered
-// in LDS (codes: 64 bytes per row padded to 80, which makes the 16-byte
-// fragment reads of 8 consecutive rows hit distinct banks; scales: 8 bytes
-// per row).  Global loads for chunk c + 2 are issued while chunk c is
-// computed, and stored to LDS during chunk c + 1.
+// in LDS: codes 64 bytes per row padded to 72 (the 8-byte fragment reads of
+// 32 consecutive rows then hit distinct banks), expanded scales as
+// [block][row] dwords with each block's 256 rows padded by 32 bytes (the two
+// half-waves read disjoint banks).  Scales are expanded once, while staging.
 //
-// K order.  The sum over k may be taken in any order as long as A and B use
-// the same one.  In half-chunk u (64 elements) lane (r, h) (r = lane % 32,
-// h = lane / 32) owns elements [64h + 32u, 64h + 32u + 32) of its row -- one
-// 16-byte LDS read -- and MFMA step t (0..3) takes its elements
-// [.. + 8t, .. + 8t + 8) (one code dword).  So each MFMA sees two 16-blocks
-// (one per half-wave), each dequantized with its own scale before the
-// multiply.
+// Pipeline.  Lane (r, h) (r = lane % 32, h = lane / 32) owns K elements
+// [64h + 16b, 64h + 16b + 16) of each chunk row in block-step b (0..3): one
+// 16-block, one expanded scale, two MFMA steps of 8 elements.  A and B use
+// the same K order, so the dot products are unchanged.  Per MFMA step the
+// kernel issues 16 MFMAs on the current fragments while it dequantizes the
+// next step's fragments (2 register sets); LDS reads run one block-step
+// ahead (2 sets).  Staging of chunk c + 1 (LDS writes from registers) and
+// the global loads of chunk c + 2 run inside chunk c's MFMA stream, and the
+// one barrier per chunk sits before its last block-step, whose operands are
+// already in registers: after it the waves read chunk c + 1's first block
+// while their last MFMAs of chunk c issue.
 //
 // Tile order.  Consecutive workgroup ids are dispatched round-robin over
 // the 8 XCDs, each with its own L2.  The id is remapped so that each XCD
@@ -58,41 +64,49 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kThreads = 256;
-constexpr int kCodeBytes = kBK / 2;            // 64 code bytes per row per chunk
-constexpr int kCodeStride = kCodeBytes + 16;   // padded LDS row stride
-constexpr int kScaleBytes = kBK / 16;          // 8 scale bytes per row per chunk
+constexpr int kCodeStride = kBK / 2 + 8;       // 64 code bytes per row, padded to 72
 constexpr int kCodesA = 0;
 constexpr int kCodesB = kCodesA + kBM * kCodeStride;
-constexpr int kScalesA = kCodesB + kBN * kCodeStride;
-constexpr int kScalesB = kScalesA + kBM * kScaleBytes;
-constexpr int kStage = kScalesB + kBN * kScaleBytes;  // 45056 bytes
+constexpr int kScaleBlockStride = kBM * 4 + 32;       // one block's 256 rows, padded
+constexpr int kScalesA = kCodesB + kBN * kCodeStride;  // [8 blocks][256 rows] dwords
+constexpr int kScalesB = kScalesA + 8 * kScaleBlockStride;
+constexpr int kStage = kScalesB + 8 * kScaleBlockStride;  // 53760 bytes
 constexpr int kLut = 2 * kStage;
-constexpr int kSmem = kLut + 256 * 8;
+constexpr int kSmem = kLut + 256 * 4;
 constexpr int kGroupM = 4;  // tile rows per group in the tile order
 
-struct ScalePair {
-    float cvt;      // 2^E, consumed by the convert instruction (exponent only)
-    f16x2_t mult;   // integer mantissa factor in both halves
-};
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100,
+              kSchedDsWrite = 0x200, kSchedVmemRead = 0x020;
+
+// Expanded scale of one UE5M3 byte c = (e, f): a dword whose fp32 exponent
+// field is max(e, 1) + 105 (the convert applies 2^(max(e,1) - 22)) and whose
+// low half is the fp16 mantissa factor m = 8 + f (normal) or f (subnormal),
+// NaN for 0xFF.  q * 2^(max(e,1)-22) * m = q * s / 16 exactly.
+__device__ __forceinline__ uint32_t expand_scale(uint32_t c) {
+    const uint32_t e = c >> 3, f = c & 7u;
+    const uint32_t eb = e > 0u ? e : 1u;
+    const _Float16 m = c == kUe5m3Nan ? (_Float16)__builtin_nanf("") : (_Float16)(float)(e > 0u ? 8u + f : f);
+    uint16_t mb;
+    __builtin_memcpy(&mb, &m, 2);
+    return ((eb + 105u) << 23) | (uint32_t)mb;
+}
 
 // 8 E2M1 codes (one dword; element k in nibble k) -> 8 fp16 values q*s/16.
-__device__ __forceinline__ f16x8_t dequant8(uint32_t w, const ScalePair& s) {
-    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.cvt, 0) * s.mult;
-    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.cvt, 1) * s.mult;
-    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.cvt, 2) * s.mult;
-    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.cvt, 3) * s.mult;
+__device__ __forceinline__ f16x8_t dequant8(uint32_t w, uint32_t S) {
+    const float sc = __uint_as_float(S);
+    const uint16_t mb = (uint16_t)S;
+    _Float16 m;
+    __builtin_memcpy(&m, &mb, 2);
+    const f16x2_t mm = {m, m};
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0) * mm;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1) * mm;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2) * mm;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3) * mm;
     f16x8_t out;
     out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
     out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
     return out;
-}
-
-__device__ __forceinline__ ScalePair lut_entry(const uint8_t* smem, uint32_t code) {
-    const uint2 v = *reinterpret_cast<const uint2*>(smem + kLut + 8 * code);
-    ScalePair s;
-    s.cvt = __uint_as_float(v.x);
-    __builtin_memcpy(&s.mult, &v.y, 4);
-    return s;
 }
 
 // Workgroup id -> (tile row, tile col), XCD-aware and grouped.
@@ -108,6 +122,48 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
     tn = (id % width) / rows;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// One 16-byte unit (32 codes) of a row's K chunk starting at k0: part p
+// covers elements [k0 + 32p, k0 + 32p + 32).  Unaligned K (a multiple of 16
+// only): each 16-element half is clamped into the row; halves past K are
+// zeroed through their scale.
+template <bool ALIGNED>
+__device__ __forceinline__ u32x4 load_unit(const uint8_t* row, int64_t K, int64_t k0, int part) {
+    if (ALIGNED) return *reinterpret_cast<const u32x4*>(row + k0 / 2 + 16 * part);
+    const int64_t ka = min(k0 + 32 * part, K - 16), kb = min(k0 + 32 * part + 16, K - 16);
+    const u32x2 x = *reinterpret_cast<const u32x2*>(row + ka / 2);
+    const u32x2 y = *reinterpret_cast<const u32x2*>(row + kb / 2);
+    return u32x4{x.x, x.y, y.x, y.y};
+}
+
+// The 8 scale bytes of a row's K chunk (block index b0 = k0 / 16); bytes
+// past the row's kblocks blocks are 0.
+template <bool ALIGNED>
+__device__ __forceinline__ u32x2 load_scales(const uint8_t* row, int64_t kblocks, int64_t b0) {
+    if (ALIGNED) return *reinterpret_cast<const u32x2*>(row + b0);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t v = row[min(b0 + j, kblocks - 1)];
+        w[j >> 2] |= (b0 + j < kblocks ? v : 0u) << (8 * (j & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// One lane's operands for one block-step (16 elements of K per row): the
+// code dwords of its 4 A rows and 4 B rows, and their expanded scales.
+struct BlockStep {
+    uint2 ca[4], cb[4];
+    uint32_t sa[4], sb[4];
+};
+
+struct Frags {
+    f16x8_t a[4], b[4];
+};
+
 template <bool ALIGNED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -115,24 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ b_scales, const float* __restrict__ b_ts, int64_t M, int64_t N,
     int64_t K, float* __restrict__ C) {
     __shared__ __align__(16) uint8_t smem[kSmem];
+    uint32_t* lut = reinterpret_cast<uint32_t*>(smem + kLut);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int r = lane & 31, h = lane >> 5;
 
-    // scale byte -> (2^E, m) table
-    {
-        const uint32_t c = (uint32_t)tid;
-        const uint32_t e = c >> 3, f = c & 7u;
-        const uint32_t eb = e > 0u ? e : 1u;
-        const uint32_t cvt_bits = (eb + 105u) << 23;  // 2^(max(e,1) - 22)
-        const _Float16 m = c == kUe5m3Nan ? (_Float16)__builtin_nanf("")
-                                          : (_Float16)(float)(e > 0u ? 8u + f : f);
-        uint16_t mb;
-        __builtin_memcpy(&mb, &m, 2);
-        *reinterpret_cast<uint2*>(smem + kLut + 8 * c) = make_uint2(cvt_bits, (uint32_t)mb * 0x10001u);
-    }
+    lut[tid] = expand_scale((uint32_t)tid);
 
     int tm, tn;
     tile_of((int)((M + kBM - 1) / kBM), (int)((N + kBN - 1) / kBN), tm, tn);
@@ -140,82 +186,99 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const int64_t kbytes = K / 2, kblocks = K / 16;
     const int nchunks = (int)((K + kBK - 1) / kBK);
 
-    // ---- global -> registers -> LDS staging
-    // codes: 256 rows x 64 bytes per operand = 1024 16-byte units, 4 per thread
-    // scales: 256 rows x 8 bytes per operand, one row per thread
-    constexpr int kUnits = ALIGNED ? 4 : 8;  // 16-byte or 8-byte code units
-    uint4 ra[ALIGNED ? 4 : 1], rb[ALIGNED ? 4 : 1];
-    uint2 ra8[ALIGNED ? 1 : 8], rb8[ALIGNED ? 1 : 8];
-    uint2 rsa, rsb;
+    // ---- staging: global -> registers -> LDS.  Every load is unconditional
+    // (rows clamped into the operand, K offsets into the row); rows outside
+    // the operand and blocks past K get scale byte 0, whose factor m = 0 makes
+    // them dequantize to exactly 0.  Thread tid stages 16-byte units
+    // tid + 256 i (i = 0..3) of each operand's 256 x 64 code bytes (row
+    // unit / 4, part unit % 4) and the 8 scale bytes of row tid.  The staging
+    // registers are plain vector values (no arrays), so they stay in VGPRs.
+    u32x4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+    u32x2 rsa, rsb;
+    u32x8 ea, eb;
+    const bool a_valid = m0 + tid < M, b_valid = n0 + tid < N;
+    const int64_t a_srow = a_valid ? m0 + tid : M - 1, b_srow = b_valid ? n0 + tid : N - 1;
+    const int srow = tid >> 2, spart = tid & 3;  // unit tid + 256 i: row srow + 64 i
+    const uint8_t* a_rows[4];
+    const uint8_t* b_rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a_rows[i] = a_codes + min(m0 + srow + 64 * i, M - 1) * kbytes;
+        b_rows[i] = b_codes + min(n0 + srow + 64 * i, N - 1) * kbytes;
+    }
+    const uint8_t* a_srow_p = a_scales + a_srow * kblocks;
+    const uint8_t* b_srow_p = b_scales + b_srow * kblocks;
 
-    auto gload = [&](int chunk) {
+    auto gload = [&](int chunk) __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)chunk * kBK;
-        if (ALIGNED) {
+        ra0 = load_unit<ALIGNED>(a_rows[0], K, k0, spart);
+        ra1 = load_unit<ALIGNED>(a_rows[1], K, k0, spart);
+        ra2 = load_unit<ALIGNED>(a_rows[2], K, k0, spart);
+        ra3 = load_unit<ALIGNED>(a_rows[3], K, k0, spart);
+        rb0 = load_unit<ALIGNED>(b_rows[0], K, k0, spart);
+        rb1 = load_unit<ALIGNED>(b_rows[1], K, k0, spart);
+        rb2 = load_unit<ALIGNED>(b_rows[2], K, k0, spart);
+        rb3 = load_unit<ALIGNED>(b_rows[3], K, k0, spart);
+        rsa = load_scales<ALIGNED>(a_srow_p, kblocks, k0 / 16) & (a_valid ? ~0u : 0u);
+        rsb = load_scales<ALIGNED>(b_srow_p, kblocks, k0 / 16) & (b_valid ? ~0u : 0u);
+    };
+    auto lstore_codes = [&](uint8_t* base) __attribute__((always_inline)) {
+        // rows are 8-byte aligned (72-byte stride): two 8-byte stores per unit
+        uint8_t* pa = base + kCodesA + srow * kCodeStride + 16 * spart;
+        uint8_t* pb = base + kCodesB + srow * kCodeStride + 16 * spart;
+        auto st = [](uint8_t* p, u32x4 v) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x2*>(p) = v.xy;
+            *reinterpret_cast<u32x2*>(p + 8) = v.zw;
+        };
+        st(pa + 0 * 64 * kCodeStride, ra0);
+        st(pa + 1 * 64 * kCodeStride, ra1);
+        st(pa + 2 * 64 * kCodeStride, ra2);
+        st(pa + 3 * 64 * kCodeStride, ra3);
+        st(pb + 0 * 64 * kCodeStride, rb0);
+        st(pb + 1 * 64 * kCodeStride, rb1);
+        st(pb + 2 * 64 * kCodeStride, rb2);
+        st(pb + 3 * 64 * kCodeStride, rb3);
+    };
+    auto lut_fetch = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int u = tid + kThreads * i;
-                const int row = u >> 2, part = u & 3;
-                const int64_t off = k0 / 2 + 16 * part;
-                ra[i] = m0 + row < M ? *reinterpret_cast<const uint4*>(a_codes + (m0 + row) * kbytes + off)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-                rb[i] = n0 + row < N ? *reinterpret_cast<const uint4*>(b_codes + (n0 + row) * kbytes + off)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-            }
-            rsa = m0 + tid < M ? *reinterpret_cast<const uint2*>(a_scales + (m0 + tid) * kblocks + k0 / 16)
-                               : make_uint2(0u, 0u);
-            rsb = n0 + tid < N ? *reinterpret_cast<const uint2*>(b_scales + (n0 + tid) * kblocks + k0 / 16)
-                               : make_uint2(0u, 0u);
-        } else {
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t wa = j < 4 ? rsa.x : rsa.y, wb = j < 4 ? rsb.x : rsb.y;
+            ea[j] = lut[(wa >> (8 * (j & 3))) & 0xFFu];
+            eb[j] = lut[(wb >> (8 * (j & 3))) & 0xFFu];
+        }
+    };
+    auto lstore_scales = [&](uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int u = tid + kThreads * i;
-                const int row = u >> 3, part = u & 7;
-                const int64_t gk = k0 + 16 * part;
-                const bool kin = gk < K;
-                ra8[i] = kin && m0 + row < M
-                             ? *reinterpret_cast<const uint2*>(a_codes + (m0 + row) * kbytes + gk / 2)
-                             : make_uint2(0u, 0u);
-                rb8[i] = kin && n0 + row < N
-                             ? *reinterpret_cast<const uint2*>(b_codes + (n0 + row) * kbytes + gk / 2)
-                             : make_uint2(0u, 0u);
-            }
-            uint32_t sa[2] = {0u, 0u}, sb[2] = {0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t blk = k0 / 16 + j;
-                if (blk < kblocks) {
-                    if (m0 + tid < M) sa[j >> 2] |= (uint32_t)a_scales[(m0 + tid) * kblocks + blk] << (8 * (j & 3));
-                    if (n0 + tid < N) sb[j >> 2] |= (uint32_t)b_scales[(n0 + tid) * kblocks + blk] << (8 * (j & 3));
-                }
-            }
-            rsa = make_uint2(sa[0], sa[1]);
-            rsb = make_uint2(sb[0], sb[1]);
+        for (int j = 0; j < 8; ++j) {
+            *reinterpret_cast<uint32_t*>(base + kScalesA + j * kScaleBlockStride + tid * 4) = ea[j];
+            *reinterpret_cast<uint32_t*>(base + kScalesB + j * kScaleBlockStride + tid * 4) = eb[j];
         }
     };
 
-    auto lstore = [&](int stage) {
-        uint8_t* base = smem + stage * kStage;
-        if (ALIGNED) {
+    // ---- per-lane LDS read offsets.  Lane (r, h) covers K elements
+    // [64h + 16b, 64h + 16b + 16) of every chunk row in block-step b (its
+    // block 4h + b), 8 of them per MFMA step.
+    const int a_code_off = kCodesA + (wm * 128 + r) * kCodeStride + 32 * h;
+    const int b_code_off = kCodesB + (wn * 128 + r) * kCodeStride + 32 * h;
+    const int a_sc_off = kScalesA + 4 * h * kScaleBlockStride + (wm * 128 + r) * 4;
+    const int b_sc_off = kScalesB + 4 * h * kScaleBlockStride + (wn * 128 + r) * 4;
+
+    auto read_bs = [&](BlockStep& bs, const uint8_t* base, int b) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int u = tid + kThreads * i;
-                const int row = u >> 2, part = u & 3;
-                *reinterpret_cast<uint4*>(base + kCodesA + row * kCodeStride + 16 * part) = ra[i];
-                *reinterpret_cast<uint4*>(base + kCodesB + row * kCodeStride + 16 * part) = rb[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int u = tid + kThreads * i;
-                const int row = u >> 3, part = u & 7;
-                *reinterpret_cast<uint2*>(base + kCodesA + row * kCodeStride + 8 * part) = ra8[i];
-                *reinterpret_cast<uint2*>(base + kCodesB + row * kCodeStride + 8 * part) = rb8[i];
-            }
+        for (int g = 0; g < 4; ++g) {
+            bs.ca[g] = *reinterpret_cast<const uint2*>(base + a_code_off + g * 32 * kCodeStride + 8 * b);
+            bs.cb[g] = *reinterpret_cast<const uint2*>(base + b_code_off + g * 32 * kCodeStride + 8 * b);
+            bs.sa[g] = *reinterpret_cast<const uint32_t*>(base + a_sc_off + b * kScaleBlockStride + g * 128);
+            bs.sb[g] = *reinterpret_cast<const uint32_t*>(base + b_sc_off + b * kScaleBlockStride + g * 128);
         }
-        *reinterpret_cast<uint2*>(base + kScalesA + tid * kScaleBytes) = rsa;
-        *reinterpret_cast<uint2*>(base + kScalesB + tid * kScaleBytes) = rsb;
     };
-    (void)kUnits;
+    auto dequant = [&](Frags& f, const BlockStep& bs, int t1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f.a[g] = dequant8(t1 ? bs.ca[g].y : bs.ca[g].x, bs.sa[g]);
+            f.b[g] = dequant8(t1 ? bs.cb[g].y : bs.cb[g].x, bs.sb[g]);
+        }
+    };
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -226,51 +289,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     if (nchunks > 0) {
+        __syncthreads();  // table visible
         gload(0);
-        lstore(0);
-        if (nchunks > 1) gload(1);
-    }
-    __syncthreads();
+        lut_fetch();
+        lstore_codes(smem);
+        lstore_scales(smem);
+        gload(min(1, nchunks - 1));
+        __syncthreads();
 
-    for (int c = 0; c < nchunks; ++c) {
-        const uint8_t* base = smem + (c & 1) * kStage;
-#pragma unroll 1
-        for (int u = 0; u < 2; ++u) {
-            uint4 ca[4], cb[4];
-            ScalePair sa[4][2], sb[4][2];
+        BlockStep bsr[2];
+        Frags fr[2];
+        read_bs(bsr[0], smem, 0);
+        dequant(fr[0], bsr[0], 0);
+
+        for (int c = 0; c < nchunks; ++c) {
+            uint8_t* cur = smem + (c & 1) * kStage;
+            uint8_t* nxt = smem + ((c + 1) & 1) * kStage;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int arow = wm * 128 + g * 32 + r;
-                const int brow = wn * 128 + g * 32 + r;
-                ca[g] = *reinterpret_cast<const uint4*>(base + kCodesA + arow * kCodeStride + 32 * h + 16 * u);
-                cb[g] = *reinterpret_cast<const uint4*>(base + kCodesB + brow * kCodeStride + 32 * h + 16 * u);
-                const uint32_t s2a = *reinterpret_cast<const uint16_t*>(base + kScalesA + arow * kScaleBytes + 4 * h + 2 * u);
-                const uint32_t s2b = *reinterpret_cast<const uint16_t*>(base + kScalesB + brow * kScaleBytes + 4 * h + 2 * u);
-                sa[g][0] = lut_entry(smem, s2a & 0xFFu);
-                sa[g][1] = lut_entry(smem, s2a >> 8);
-                sb[g][0] = lut_entry(smem, s2b & 0xFFu);
-                sb[g][1] = lut_entry(smem, s2b >> 8);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f16x8_t fa[4], fb[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t wa = t == 0 ? ca[g].x : t == 1 ? ca[g].y : t == 2 ? ca[g].z : ca[g].w;
-                    const uint32_t wb = t == 0 ? cb[g].x : t == 1 ? cb[g].y : t == 2 ? cb[g].z : cb[g].w;
-                    fa[g] = dequant8(wa, sa[g][t >> 1]);
-                    fb[g] = dequant8(wb, sb[g][t >> 1]);
-                }
+            for (int J = 0; J < 8; ++J) {
+                const Frags& f = fr[J & 1];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+                // LDS reads one block-step ahead; the next chunk's first
+                // block-step only after the barrier
+                if (J == 0 || J == 2 || J == 4) read_bs(bsr[((J >> 1) + 1) & 1], cur, (J >> 1) + 1);
+                if (J == 6) read_bs(bsr[0], nxt, 0);
+                // staging of chunk c + 1 into the other buffer, loads of c + 2
+                if (J == 1) {
+                    lstore_codes(nxt);
+                    lut_fetch();
+                    gload(min(c + 2, nchunks - 1));
+                }
+                if (J == 2) lstore_scales(nxt);
+                // fragments of the next MFMA step
+                dequant(fr[(J + 1) & 1], bsr[((J + 1) >> 1) & 1], (J + 1) & 1);
+                // interleave: each MFMA followed by up to 5 VALU, 2 LDS and
+                // 2 global-load instructions, so the dequantization of the
+                // next step issues while the matrix core works
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
+                    if (q < 10) __builtin_amdgcn_sched_group_barrier(kSchedDsRead | kSchedDsWrite, 2, 0);
+                    if (q < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+                }
+                if (J == 5) __syncthreads();
             }
         }
-        if (c + 1 < nchunks) lstore((c + 1) & 1);
-        if (c + 2 < nchunks) gload(c + 2);
-        __syncthreads();
     }
 
     // ---- epilogue: C = (acc * 256 tsA) * tsB.  Accumulator register e of lane
