@@ -40,11 +40,14 @@ namespace ue5m3fp4 {
 
 namespace {
 
-constexpr int kTileRows = 128;
+constexpr int kTileRows = 64;
 constexpr int kTileCols = 256;
 constexpr int kThreads = 256;
+constexpr int kLdsRowBytes = kTileCols * 2;  // one bf16 tile row
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     u16x2_t x, y;
@@ -61,82 +64,119 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
+// LDS position of 16-byte unit u (8 columns) of tile row `row`: the unit
+// index is XORed with bits 4..5 of the row, so the column pass (lanes over 4
+// row blocks x 16 column pairs) reads 64 distinct banks.
+__device__ __forceinline__ int lds_offset(int row, int u) {
+    return row * kLdsRowBytes + ((u ^ (((row >> 4) & 3) << 2)) << 4);
+}
+
 struct Ctx {
     float ts, K, yK;  // K = 6 ts, yK = RN(1 / K)
     bool fastK;       // K inside the range where the refined division is exact
+    bool tinyOK;      // K >= 1: a block amax below 2^-100 gives scale code 0
 };
 
 struct BlockScale {
     uint32_t code;  // UE5M3 byte
-    float r;        // 1 / (ts * s_b); 0 for a flushed block (payload = sign only);
-                    // NaN for a NaN block; may be +Inf if ts * s_b underflows
+    float r;        // RN(1 / (ts * s_b)); 0 for code 0 (payload = sign only)
 };
 
-// General path: any amax, any tensor scale.
-__device__ __noinline__ BlockScale block_scale_general(float amax, Ctx c) {
+// Block scale by the definition (any amax, any tensor scale): IEEE division,
+// the integer encoder and decoder.  r is NaN for a NaN block.
+__device__ __noinline__ BlockScale block_scale_general(uint32_t amax16, float ts, float K) {
+    const float amax = __uint_as_float(amax16 << 16);
     BlockScale b;
-    b.code = ue5m3_encode(amax / c.K);
+    b.code = ue5m3_encode(amax / K);
     if (b.code == 0u) b.r = 0.0f;
     else if (b.code == kUe5m3Nan) b.r = __uint_as_float(0x7FC00000u);
-    else b.r = 1.0f / (c.ts * ue5m3_decode(b.code));
+    else b.r = 1.0f / (ts * ue5m3_decode(b.code));
     return b;
 }
 
-__device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits16, const Ctx& c) {
-    const float amax = __uint_as_float(amax_bits16 << 16);
-    // refined division amax / K (exact where guarded below)
+// Reciprocal table entry for scale code c: RN(1 / RN(ts * s_c)) by IEEE
+// division, 0 for code 0; NaN marks codes the fast path must not use (the
+// NaN code, and reciprocals that overflow or are NaN).
+__device__ __forceinline__ float rcp_entry(uint32_t c, float ts) {
+    if (c == 0u) return 0.0f;
+    if (c == kUe5m3Nan) return __uint_as_float(0x7FC00000u);
+    const float r = 1.0f / (ts * ue5m3_decode(c));
+    return fabsf(r) <= 3.4028235e38f ? r : __uint_as_float(0x7FC00000u);
+}
+
+// Fast block scale.  s = amax / K by the refined division (exact for
+// amax >= 2^-100 and K in [2^-100, 2^100] wherever the code depends on it:
+// quotients below 2^-100 give code 0 and above 2^100 saturate either way).
+// Normal range (s >= 2^-14, or s overflowed to NaN): keep 3 mantissa bits of
+// s, round the other 20 to nearest even, saturate at 0xFE.  Below 2^-14:
+// code = rint(s * 2^17) (0..8; 8 is the smallest normal code).  r comes
+// from the per-workgroup table.  `ok` is cleared for blocks the fast path
+// cannot take (Inf/NaN amax, tiny amax with K < 1, NaN table entries).
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax16, const Ctx& c,
+                                                  const float* __restrict__ rlut, bool& ok) {
+    const float amax = __uint_as_float(amax16 << 16);
     const float q = amax * c.yK;
     const float rr = __builtin_fmaf(-c.K, q, amax);
     const float s = __builtin_fmaf(rr, c.yK, q);
-    // UE5M3 normal range: keep 3 mantissa bits, round the other 20 to nearest even
     const uint32_t sb = __float_as_uint(s);
-    const uint32_t rounded = (sb + 0x7FFFFu + ((sb >> 20) & 1u)) >> 20;
-    const uint32_t code = min(rounded - (112u << 3), kUe5m3MaxCode);  // rebias 127 -> 15
-    const float sval = __uint_as_float((code + (112u << 3)) << 20);   // exact UE5M3 value
-    const float d = c.ts * sval;
-    const bool fast = c.fastK && amax >= 0x1p-100f && s >= 0x1p-14f && s <= 0x1p100f &&
-                      d >= 0x1p-100f && d <= 0x1p100f;
-    if (__builtin_expect(fast, 1)) {
-        const float y = __builtin_amdgcn_rcpf(d);
-        const float e = __builtin_fmaf(-d, y, 1.0f);
-        BlockScale b;
-        b.code = code;
-        b.r = __builtin_fmaf(e, y, y);
-        return b;
-    }
-    return block_scale_general(amax, c);
+    const uint32_t rounded = min((sb + 0x7FFFFu + ((sb >> 20) & 1u)) >> 20, (112u << 3) + kUe5m3MaxCode);
+    // clamped to [0, 8] so the conversion is defined for every s
+    const uint32_t code_s = (uint32_t)fminf(fmaxf(__builtin_rintf(s * 0x1p17f), 0.0f), 8.0f);
+    const uint32_t code_n = (rounded - (112u << 3)) & 0xFFu;
+    const uint32_t sub = s < 0x1p-14f ? ~0u : 0u;
+    BlockScale b;
+    b.code = (code_s & sub) | (code_n & ~sub);
+    b.r = rlut[b.code];
+    ok = ok & (amax16 < 0x7F80u) & ((amax16 >= 0x0D80u) | c.tinyOK) & (b.r == b.r);
+    return b;
 }
 
-// Payload nibble of one element by the definition (software path): RNE or SR
-// on |x * r|; a NaN block scale leaves only the sign bit.
+// 8 fp32 values -> 8 E2M1 nibbles (element k in nibble k).
+// RNE: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1
+// exactly as the nearest-even definition does, sign included (checked on
+// gfx950 for all 2^32 non-NaN inputs).  SR: magnitude index from formats.hpp.
 template <bool SR>
-__device__ __forceinline__ uint32_t element_code(float x, const BlockScale& b, uint32_t u16) {
-    const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
-    const float a = fabsf(x * b.r);
-    const uint32_t idx = SR ? e2m1_sr_index(a, u16) : e2m1_rne_index(a);
-    return sign | (b.code == kUe5m3Nan ? 0u : idx);
-}
-
-// 8 fp32 elements (already unpacked) -> 8 nibbles, element k in nibble k.
-template <bool SR>
-__device__ __forceinline__ uint32_t encode8(const float (&x)[8], const BlockScale& b,
-                                           const U32x4& rnd) {
-    if (!SR && __builtin_expect(b.r <= 3.4028235e38f, 1)) {
+__device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rnd) {
+    if (!SR) {
         uint32_t p = 0u;
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[0] * b.r, x[1] * b.r, 1.0f, 0);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[2] * b.r, x[3] * b.r, 1.0f, 1);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[4] * b.r, x[5] * b.r, 1.0f, 2);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[6] * b.r, x[7] * b.r, 1.0f, 3);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], 1.0f, 0);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], 1.0f, 1);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], 1.0f, 2);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
         return p;
     }
     uint32_t p = 0u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) p |= element_code<SR>(x[k], b, SR ? sr_u16(rnd, k) : 0u) << (4 * k);
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
+        p |= (sign | e2m1_sr_index(fabsf(v[k]), sr_u16(rnd, k))) << (4 * k);
+    }
     return p;
 }
 
-__device__ __forceinline__ uint32_t comp(const uint4& v, int k) {
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+// Software element codes for blocks from block_scale_general: the same
+// definition with the NaN-block rule (sign only) and any r.  The 8 bf16
+// inputs arrive as 4 words (element 2i in the low half of word i).
+template <bool SR>
+__device__ __noinline__ uint32_t encode8_general(u32x4 w, uint32_t code, float r, U32x4 rnd) {
+    uint32_t p = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t word = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+        const float x = (k & 1) ? bf16_hi(word) : bf16_lo(word);
+        const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+        const float a = fabsf(x * r);
+        const uint32_t idx = SR ? e2m1_sr_index(a, sr_u16(rnd, k)) : e2m1_rne_index(a);
+        p |= (sign | (code == kUe5m3Nan ? 0u : idx)) << (4 * k);
+    }
+    return p;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
 template <bool ROW, bool COL, bool SR, bool AMAX>
@@ -146,144 +186,218 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
     uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
     float* __restrict__ amax_inout) {
-    const int tx = threadIdx.x & 31;
-    const int ty = threadIdx.x >> 5;
-    const int64_t r0 = (int64_t)blockIdx.y * kTileRows + 16 * ty;
-    const int64_t c0 = (int64_t)blockIdx.x * kTileCols + 8 * tx;
-    const bool col_ok = c0 < cols;  // cols % 16 == 0: the two lanes of a pair agree
+    __shared__ __align__(16) uint8_t tile[COL ? kTileRows * kLdsRowBytes : 16];
+    __shared__ float rlut[(ROW || COL) ? 256 : 1];
+    const int t = threadIdx.x;
+    // Grid: x over column tiles, y over row tiles.  Workgroups are dispatched
+    // round-robin over the 8 XCDs in linear order, so with a multiple of 8
+    // column tiles the vertically adjacent tiles -- which share 128-byte lines
+    // of the transposed output -- are written through the same L2.
+    const int64_t R0 = (int64_t)blockIdx.y * kTileRows, C0 = (int64_t)blockIdx.x * kTileCols;
+    const bool interior = R0 + kTileRows <= rows && C0 + kTileCols <= cols;
 
-    // ---- 16 unconditional loads (clamped addresses), zeroed outside the tensor
-    uint4 v[16];
+    // ---- loads: thread t owns 16-byte unit u = t % 32 (8 columns) of tile
+    // rows t / 32 + 8k, k = 0..7; a wave reads 2 rows x 512 bytes per load.
+    // Loads are unconditional: addresses outside the tensor are clamped to
+    // its last row / last 8 columns.  The duplicated values never reach an
+    // output (cols % 16 == 0, and rows % 16 == 0 when the transposed output
+    // is written) and cannot raise the tensor amax.
+    const int u = t & 31, rbase = t >> 5;
+    const int64_t c0 = C0 + 8 * u;
+    const bool col_ok = c0 < cols;
+    u32x4 w[8];
     {
-        const int64_t cc = col_ok ? c0 : cols - 8;
+        const uint16_t* src = x + (col_ok ? c0 : cols - 8);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t r = r0 + i < rows ? r0 + i : rows - 1;
-            v[i] = *reinterpret_cast<const uint4*>(x + r * ld + cc);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (!(col_ok && r0 + i < rows)) v[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int k = 0; k < 8; ++k) {
+            const int64_t r = min(R0 + rbase + 8 * k, rows - 1);
+            w[k] = *reinterpret_cast<const u32x4*>(src + r * ld);
         }
     }
 
-    Ctx ctx{0.0f, 0.0f, 0.0f, false};
+    Ctx ctx{0.0f, 0.0f, 0.0f, false, false};
     if (ROW || COL) {
         ctx.ts = *tensor_scale;
         ctx.K = 6.0f * ctx.ts;
         ctx.yK = 1.0f / ctx.K;
         ctx.fastK = ctx.K >= 0x1p-100f && ctx.K <= 0x1p100f;
+        ctx.tinyOK = ctx.K >= 1.0f;
+        rlut[t] = rcp_entry((uint32_t)t, ctx.ts);
     }
 
-    // ---- amax of every row half-block and of every column pair
-    uint32_t rmax[16];
-    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+    // ---- row half-block amax (bf16 magnitude bits; NaN sorts above Inf)
+    uint32_t hmax[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t m0 = v[i].x & 0x7FFF7FFFu, m1 = v[i].y & 0x7FFF7FFFu;
-        const uint32_t m2 = v[i].z & 0x7FFF7FFFu, m3 = v[i].w & 0x7FFF7FFFu;
-        if (COL) {
-            cm[0] = pk_max_u16(cm[0], m0);
-            cm[1] = pk_max_u16(cm[1], m1);
-            cm[2] = pk_max_u16(cm[2], m2);
-            cm[3] = pk_max_u16(cm[3], m3);
-        }
-        const uint32_t m = pk_max_u16(pk_max_u16(m0, m1), pk_max_u16(m2, m3));
-        rmax[i] = max(m & 0xFFFFu, m >> 16);
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t m = pk_max_u16(pk_max_u16(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu),
+                                      pk_max_u16(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu));
+        hmax[k] = max(m & 0xFFFFu, m >> 16);
     }
-
-    uint32_t tmax = 0u;  // max |x| of this thread (bf16 magnitude bits)
+    uint32_t tmax = 0u;
     if (AMAX) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = max(tmax, rmax[i]);
+        for (int k = 0; k < 8; ++k) tmax = max(tmax, hmax[k]);
     }
 
-    // ---- row-wise output: blocks along columns
-    if (ROW) {
-        // The lane pair splits the row blocks: for rows 2k and 2k + 1, lane
-        // parity p computes the scale of row 2k + p and swaps it with its partner.
-        const uint32_t p = tx & 1;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t mine = p ? rmax[2 * k + 1] : rmax[2 * k];
-            const uint32_t other = p ? rmax[2 * k] : rmax[2 * k + 1];
-            // block amax of row 2k + p: my half of it and the partner's half
-            const BlockScale own = block_scale(max(mine, swap_pair(other)), ctx);
-            BlockScale par;
-            par.code = swap_pair(own.code);
-            par.r = __uint_as_float(swap_pair(__float_as_uint(own.r)));
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int i = 2 * k + q;
-                const BlockScale& b = (q == (int)p) ? own : par;
-                BlockScale bb;
-                bb.code = q == 0 ? (p ? par.code : own.code) : (p ? own.code : par.code);
-                bb.r = q == 0 ? (p ? par.r : own.r) : (p ? own.r : par.r);
-                (void)b;
-                const int64_t r = r0 + i;
-                U32x4 rnd;
-                if (SR) rnd = sr_words(((uint64_t)r * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
-                float xs[8];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    xs[2 * m] = bf16_lo(comp(v[i], m));
-                    xs[2 * m + 1] = bf16_hi(comp(v[i], m));
-                }
-                const uint32_t packed = encode8<SR>(xs, bb, rnd);
-                if (col_ok && r < rows) {
-                    *reinterpret_cast<uint32_t*>(row_codes + r * (cols / 2) + c0 / 2) = packed;
-                    if (p == 0) row_scales[r * (cols / 16) + c0 / 16] = (uint8_t)bb.code;
-                }
-            }
-        }
-        if (COL) {
-            // Opaque to the optimizer: stops it from keeping the unpacked
-            // values of the row pass alive for reuse in the column pass (that
-            // doubles the live registers).  No instruction is emitted.
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
-        }
-    }
-
-    // ---- transposed output: blocks along rows, one whole block per column
     if (COL) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t mj = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
-            const BlockScale b = block_scale(mj, ctx);
-            const int64_t c = c0 + j;
-            U32x4 rnd0, rnd1;
-            if (SR) {
-                const uint64_t n0 = ((uint64_t)c * (uint64_t)rows + (uint64_t)r0) >> 3;
-                rnd0 = sr_words(n0, offset, 1u, seed);
-                rnd1 = sr_words(n0 + 1u, offset, 1u, seed);
-            }
-            float lo[8], hi[8];
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<u32x4*>(tile + lds_offset(rbase + 8 * k, u)) = w[k];
+    }
+    if (ROW || COL) __syncthreads();  // reciprocal table (and tile) visible
+
+    // ---- row-wise output.  The lane pair (t, t ^ 1) shares each 16-block;
+    // lane parity p computes the scales of rows k = 2m + p and the pair swaps
+    // them.
+    if (ROW) {
+        const uint32_t p = t & 1;
+        uint32_t code[8];
+        float rr[8];
+        bool ok = ctx.fastK;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t wl = comp(v[i], j >> 1), wh = comp(v[8 + i], j >> 1);
-                lo[i] = (j & 1) ? bf16_hi(wl) : bf16_lo(wl);
-                hi[i] = (j & 1) ? bf16_hi(wh) : bf16_lo(wh);
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t mine = p ? hmax[2 * m + 1] : hmax[2 * m];
+            const uint32_t other = p ? hmax[2 * m] : hmax[2 * m + 1];
+            const BlockScale own = block_scale(max(mine, swap_pair(other)), ctx, rlut, ok);
+            const uint32_t pc = swap_pair(own.code);
+            const float pr = __uint_as_float(swap_pair(__float_as_uint(own.r)));
+            code[2 * m] = p ? pc : own.code;
+            rr[2 * m] = p ? pr : own.r;
+            code[2 * m + 1] = p ? own.code : pc;
+            rr[2 * m + 1] = p ? own.r : pr;
+        }
+        // both lanes of the pair must take the same path; the exchange runs in
+        // every lane (a short-circuit && would skip it where ok is false)
+        const uint32_t ok_bit = ok ? 1u : 0u;
+        const bool pair_ok = (ok_bit & swap_pair(ok_bit)) != 0u;
+        uint32_t packed[8];
+        if (__builtin_expect(pair_ok, 1)) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float v[8];
+                unpack8(w[k], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = v[e] * rr[k];
+                U32x4 rnd;
+                if (SR) rnd = sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3,
+                                       offset, 0u, seed);
+                packed[k] = encode8<SR>(v, rnd);
             }
-            const uint32_t plo = encode8<SR>(lo, b, rnd0);
-            const uint32_t phi = encode8<SR>(hi, b, rnd1);
-            if (col_ok && r0 < rows) {
-                *reinterpret_cast<uint2*>(col_codes + c * (rows / 2) + r0 / 2) = make_uint2(plo, phi);
-                col_scales[c * (rows / 16) + r0 / 16] = (uint8_t)b.code;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t blk = max(hmax[k], swap_pair(hmax[k]));  // both lanes active here
+                const BlockScale b = block_scale_general(blk, ctx.ts, ctx.K);
+                U32x4 rnd;
+                if (SR) rnd = sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3,
+                                       offset, 0u, seed);
+                packed[k] = encode8_general<SR>(w[k], b.code, b.r, rnd);
+                code[k] = b.code;
+            }
+        }
+        uint8_t* pc = row_codes + (R0 + rbase) * (cols / 2) + c0 / 2;
+        uint8_t* ps = row_scales + (R0 + rbase) * (cols / 16) + c0 / 16;
+        const int64_t cstep = 8 * (cols / 2), sstep = 8 * (cols / 16);
+        if (interior) {
+            // both lanes of a pair store the block's scale byte (same value)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+                ps[k * sstep] = (uint8_t)code[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (col_ok && R0 + rbase + 8 * k < rows) {
+                    *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+                    if (p == 0) ps[k * sstep] = (uint8_t)code[k];
+                }
+            }
+        }
+    }
+
+    // ---- transposed output: lane (rb, cp) = (lane % 4, lane / 4) of wave w
+    // quantizes columns 2j, 2j + 1 (j = 16 s + cp, slot s = w + 4 pass) over
+    // tile rows 16 rb .. 16 rb + 15: one 16-block per column.  The 4 lanes of
+    // a column write its 64 tile rows as 32 contiguous bytes.
+    if (COL) {
+        const int lane = t & 63, wv = t >> 6;
+        const int rb = lane & 3, cp = lane >> 2;
+        const int64_t r0 = R0 + 16 * rb;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int j = 16 * (wv + 4 * pass) + cp;  // column pair within the tile
+            const int64_t ca = C0 + 2 * j;
+            uint32_t cw[16];
+            const uint8_t* src = tile + lds_offset(16 * rb, j >> 2) + 4 * (j & 3);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(src + i * kLdsRowBytes);
+            uint32_t m2 = 0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m2 = pk_max_u16(m2, cw[i] & 0x7FFF7FFFu);
+            bool ok = ctx.fastK;
+            const BlockScale ba = block_scale(m2 & 0xFFFFu, ctx, rlut, ok);
+            const BlockScale bb = block_scale(m2 >> 16, ctx, rlut, ok);
+            uint32_t pa[2], pb[2];
+            U32x4 rnd[4];
+            if (SR) {
+                const uint64_t na = ((uint64_t)ca * (uint64_t)rows + (uint64_t)r0) >> 3;
+                const uint64_t nb = ((uint64_t)(ca + 1) * (uint64_t)rows + (uint64_t)r0) >> 3;
+                rnd[0] = sr_words(na, offset, 1u, seed);
+                rnd[1] = sr_words(na + 1u, offset, 1u, seed);
+                rnd[2] = sr_words(nb, offset, 1u, seed);
+                rnd[3] = sr_words(nb + 1u, offset, 1u, seed);
+            }
+            uint32_t code_a = ba.code, code_b = bb.code;
+            if (__builtin_expect(ok, 1)) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float va[8], vb[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        va[i] = bf16_lo(cw[8 * hh + i]) * ba.r;
+                        vb[i] = bf16_hi(cw[8 * hh + i]) * bb.r;
+                    }
+                    pa[hh] = encode8<SR>(va, rnd[hh]);
+                    pb[hh] = encode8<SR>(vb, rnd[2 + hh]);
+                }
+            } else {
+                const BlockScale ga = block_scale_general(m2 & 0xFFFFu, ctx.ts, ctx.K);
+                const BlockScale gb = block_scale_general(m2 >> 16, ctx.ts, ctx.K);
+                code_a = ga.code;
+                code_b = gb.code;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    // words holding (column a, column b) of 8 rows -> per-column words
+                    uint32_t la[4], lb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t w0 = cw[8 * hh + 2 * i], w1 = cw[8 * hh + 2 * i + 1];
+                        la[i] = (w0 & 0xFFFFu) | (w1 << 16);
+                        lb[i] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+                    }
+                    pa[hh] = encode8_general<SR>(u32x4{la[0], la[1], la[2], la[3]}, ga.code, ga.r, rnd[hh]);
+                    pb[hh] = encode8_general<SR>(u32x4{lb[0], lb[1], lb[2], lb[3]}, gb.code, gb.r, rnd[2 + hh]);
+                }
+            }
+            if (interior || (ca < cols && r0 < rows)) {
+                *reinterpret_cast<u32x2*>(col_codes + ca * (rows / 2) + r0 / 2) = u32x2{pa[0], pa[1]};
+                *reinterpret_cast<u32x2*>(col_codes + (ca + 1) * (rows / 2) + r0 / 2) = u32x2{pb[0], pb[1]};
+                col_scales[ca * (rows / 16) + r0 / 16] = (uint8_t)code_a;
+                col_scales[(ca + 1) * (rows / 16) + r0 / 16] = (uint8_t)code_b;
             }
         }
     }
 
     // ---- tensor amax: wave reduction; the atomic is issued only when the
     // wave's max exceeds the running value already there.  Atomics on one
-    // address from every wave serialize across the XCDs and would cost more
-    // than the whole quantization; a max only grows, so skipping when the
-    // (possibly stale) value read is already >= ours is exact.
+    // address from every wave serialize across the XCDs; a max only grows,
+    // so skipping when the (possibly stale) value read is already >= ours is
+    // exact.
     if (AMAX) {
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, s));
-        if ((threadIdx.x & 63) == 0 && tmax != 0u) {
+        if ((t & 63) == 0 && tmax != 0u) {
             unsigned int* dst = reinterpret_cast<unsigned int*>(amax_inout);
             const unsigned int seen = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((tmax << 16) > seen) atomicMax(dst, tmax << 16);
