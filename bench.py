@@ -13,8 +13,18 @@ divided by the measured step time, in TFLOP/s.  `roofline` is for the GEMM
 kernel (the dominant kernel): algorithmic flops per launch over its average
 launch time, measured with HIP events on the stream it runs on, against the
 fp16 dense MFMA peak (the kernel feeds exact fp16 dequantizations to fp16
-MFMA; fp16 and bf16 share the 2.5 PFLOP/s dense peak).  `quantize` reports the quantizer's GB/s against HBM peak.
+MFMA; fp16 and bf16 share the 2.5 PFLOP/s dense peak).  Its `traffic` is the
+HBM bytes per launch from the committed rocprofv3 counter summary of this
+command, reported only while the GEMM source still matches the one profiled.
+`quantize` reports the quantizer's GB/s inside the step (round-to-nearest
+and stochastic calls separately) and, as `quantize_activations`, on its own
+over the 8192 x 4096 heavy-tailed activation workload with 8 rotating
+HBM-resident buffer sets (the quantizer's bandwidth roofline).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+
+`--copy-calibration` instead runs a plain 256 MiB device copy, whose
+FETCH_SIZE / WRITE_SIZE counter readings give the scale factors that turn
+those counters into bytes.
 """
 
 import argparse
@@ -41,7 +51,44 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--period", type=int, default=1, help="tensor-scale refresh period")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-quantize-only", action="store_true",
+                   help="skip the stand-alone quantizer measurement")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a 256 MiB device copy (counter calibration)")
     return p.parse_args()
+
+
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_nt_kernel_ffn_pair_counters.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when the GEMM source changed since the counters were taken."""
+    import hashlib
+
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            prof = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if prof.get("gemm_source_sha256") != digest:
+        return None
+    return float(prof["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+
+    n = 256 * 1024 * 1024 // 4  # 256 MiB of fp32
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 class Tensor:
@@ -65,6 +112,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -116,7 +167,7 @@ def main():
                 if e0:
                     e1 = ev()
                     e1.record()
-                    timing["quantize"].append((e0, e1, t.elems))
+                    timing["quantize"].append((e0, e1, t.elems, t.rounding))
             for fn, a, b, c in ((lib.gemm_fprop, X.row, W.row, Y), (lib.gemm_dgrad, D.row, W.col, dX),
                                 (lib.gemm_wgrad, D.col, X.col, dW)):
                 e0 = ev() if timing is not None else None
@@ -150,12 +201,18 @@ def main():
 
     gemm_ms = [a.elapsed_time(b) for a, b, _ in timing["gemm"]]
     gemm_fl = [f for _, _, f in timing["gemm"]]
-    q_ms = [a.elapsed_time(b) for a, b, _ in timing["quantize"]]
-    q_el = [n for _, _, n in timing["quantize"]]
     gemm_avg_ms = float(np.mean(gemm_ms))
     gemm_tflops = float(np.sum(gemm_fl) / (np.sum(gemm_ms) * 1e-3) / 1e12)
-    q_gbs = float(np.sum(q_el) * QUANT_BYTES_PER_ELEM / (np.sum(q_ms) * 1e-3) / 1e9)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    def q_stats(rounding):
+        sel = [(a.elapsed_time(b), n) for a, b, n, rnd in timing["quantize"] if rnd == rounding]
+        ms = float(sum(m for m, _ in sel))
+        gbs = sum(n for _, n in sel) * QUANT_BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+        return {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "avg_launch_ms": round(ms / len(sel), 4), "launches_per_step": len(sel) // args.steps}
+
+    traffic = gemm_traffic()
 
     result = {
         "metric": METRIC,
@@ -182,15 +239,65 @@ def main():
                      "achieved": round(gemm_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                      "avg_launch_ms": round(gemm_avg_ms, 4),
-                     "flop_per_launch": gemm_fl[0], "traffic": None},
-        "quantize": {"achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-                     "avg_launch_ms": round(float(np.mean(q_ms)), 4),
-                     "bytes_per_elem": QUANT_BYTES_PER_ELEM},
+                     "flop_per_launch": gemm_fl[0],
+                     "traffic": None if traffic is None else round(traffic)},
+        "quantize": {"peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_elem": QUANT_BYTES_PER_ELEM,
+                     "rne": q_stats(lib.RNE), "sr": q_stats(lib.SR)},
     }
+    step_elems = sum(t.elems for t in tensors)
+    del layers, tensors
+    torch.cuda.empty_cache()
+    if not args.no_quantize_only:
+        result["quantize_activations"] = quantize_only(lib, torch)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(step_flops, sum(t.elems for t in tensors))
+        result["cpu_baseline"] = cpu_baseline(step_flops, step_elems)
     print(json.dumps(result), flush=True)
+
+
+def quantize_only(lib, torch):
+    """The quantizer alone on the 8192 x 4096 heavy-tailed activation workload
+    (Student-t x normal body, 16 outlier columns x100): row-wise only and
+    row-wise + transposed, round-to-nearest and stochastic, tensor amax on.
+    8 device copies of the input and 8 output sets rotate (about 840 MB) so
+    every launch reads and writes HBM, not the 256 MB cache.  GB/s counts the
+    algorithmic bytes: 2 per element read, 0.5625 per element per output."""
+    from workloads import config, sr_seed
+
+    bits = config(2)["X"]
+    rows, cols = bits.shape
+    sets = 8
+    x0 = torch.from_numpy(bits.view("int16")).cuda()
+    xs = [x0.clone() for _ in range(sets)]
+    del x0
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lib.quantize_blockscale(xs[0], None, amax=amax)
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    lib.update_tensor_scale(amax, ts, 0, 1)
+    outs = [(lib.empty_quantized(rows, cols, ts), lib.empty_quantized(cols, rows, ts)) for _ in range(sets)]
+    iters = 40
+    res = {"workload": f"activations {rows}x{cols} bf16 (heavy-tailed, outlier columns)",
+           "peak": HBM_PEAK_GBS, "unit": "GB/s", "buffer_sets": sets}
+    for name, rnd, both in (("rne_row", lib.RNE, False), ("rne_row_col", lib.RNE, True),
+                            ("sr_row", lib.SR, False), ("sr_row_col", lib.SR, True)):
+        def run(i):
+            k = i % sets
+            lib.quantize_blockscale(xs[k], ts, rnd, sr_seed(2), i, row=outs[k][0],
+                                    col=outs[k][1] if both else None, amax=amax)
+        for i in range(sets):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        nbytes = rows * cols * (2 + 0.5625 * (2 if both else 1))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes}
+    return res
 
 
 def cpu_baseline(step_flops, step_elems):
