@@ -179,6 +179,26 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
     x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
+// Workgroup id -> tile origin.  Workgroups are dispatched round-robin over
+// the 8 XCDs, each with its own L2.  Each XCD takes a contiguous range of a
+// tile order that runs down bands of 4 tile rows, column by column: the 4
+// tiles of a band column share the 128-byte lines of the transposed output
+// (32 bytes each) and the 8 neighbouring band columns share the lines of the
+// row-wise scales, so their partial lines meet in one L2 while resident and
+// reach HBM as whole lines.
+__device__ __forceinline__ void tile_of(uint32_t tiles_r, uint32_t tiles_c, int64_t& R0, int64_t& C0) {
+    const uint32_t n = tiles_r * tiles_c;
+    uint32_t j = blockIdx.x;
+    const uint32_t per_xcd = n / 8;
+    if (j < per_xcd * 8) j = (j % 8) * per_xcd + j / 8;  // the tail keeps its id
+    const uint32_t band = j / (4 * tiles_c);
+    const uint32_t rem = j - band * 4 * tiles_c;
+    const uint32_t h = min(4u, tiles_r - 4 * band);  // rows in this band
+    const uint32_t tc = rem / h, tr = 4 * band + (rem - tc * h);
+    R0 = (int64_t)tr * kTileRows;
+    C0 = (int64_t)tc * kTileCols;
+}
+
 template <bool ROW, bool COL, bool SR, bool AMAX>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -189,11 +209,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     __shared__ __align__(16) uint8_t tile[COL ? kTileRows * kLdsRowBytes : 16];
     __shared__ float rlut[(ROW || COL) ? 256 : 1];
     const int t = threadIdx.x;
-    // Grid: x over column tiles, y over row tiles.  Workgroups are dispatched
-    // round-robin over the 8 XCDs in linear order, so with a multiple of 8
-    // column tiles the vertically adjacent tiles -- which share 128-byte lines
-    // of the transposed output -- are written through the same L2.
-    const int64_t R0 = (int64_t)blockIdx.y * kTileRows, C0 = (int64_t)blockIdx.x * kTileCols;
+    int64_t R0, C0;
+    tile_of((uint32_t)((rows + kTileRows - 1) / kTileRows), (uint32_t)((cols + kTileCols - 1) / kTileCols),
+            R0, C0);
     const bool interior = R0 + kTileRows <= rows && C0 + kTileCols <= cols;
 
     // ---- loads: thread t owns 16-byte unit u = t % 32 (8 columns) of tile
@@ -407,9 +425,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
 template <bool ROW, bool COL, bool SR, bool AMAX>
 void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.cols + kTileCols - 1) / kTileCols),
-                    (unsigned)((a.rows + kTileRows - 1) / kTileRows));
-    hipLaunchKernelGGL((quantize_kernel<ROW, COL, SR, AMAX>), grid, dim3(kThreads), 0, stream, a.x,
+    const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + kTileRows - 1) / kTileRows);
+    hipLaunchKernelGGL((quantize_kernel<ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
                        a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
                        a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
 }
