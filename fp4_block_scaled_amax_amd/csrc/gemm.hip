@@ -344,17 +344,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     // ---- epilogue: C = (acc * 256 tsA) * tsB.  Accumulator register e of lane
     // (r, h) holds row 8 * (e / 4) + 4 * h + e % 4, column r of a 32 x 32 tile.
     const float sa256 = *a_ts * 256.0f, tsb = *b_ts;
+    const int64_t row0 = m0 + wm * 128 + 4 * h, col0 = n0 + wn * 128 + r;
+    if (m0 + kBM <= M && n0 + kBN <= N) {
+        // interior tile: one row pointer per accumulator row, the 4 column
+        // tiles at immediate offsets
+        float* base = C + row0 * N + col0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 32 + r;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (row < M && col < N) C[row * N + col] = (acc[i][j][e] * sa256) * tsb;
+                float* rowp = base + (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * N;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rowp[j * 32] = (acc[i][j][e] * sa256) * tsb;
             }
-        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = col0 + j * 32;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = row0 + i * 32 + 8 * (e >> 2) + (e & 3);
+                    if (row < M && col < N) C[row * N + col] = (acc[i][j][e] * sa256) * tsb;
+                }
+            }
+    }
 }
 
 }  // namespace
