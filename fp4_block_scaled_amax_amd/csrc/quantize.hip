@@ -8,31 +8,34 @@
 // Transposition-Invariant Block Quantization" (related-papers summary): a
 // 1-D-blocked tensor and its transpose get different scales, so the
 // transposed GEMM operand is quantized again along its own axis -- here from
-// the same bf16 registers, so the input is read from HBM once.
+// the same bf16 tile, so the input is read from HBM once.
 //
-// Work decomposition.  A 256-thread workgroup owns a 128 x 256 tile; each
-// thread a 16-row x 8-column piece, loaded as 16 coalesced 16-byte row
-// segments (a wave reads 2 rows x 512 bytes per instruction).  Along a row
-// the thread holds half of a 16-element block and the partner lane (lane ^ 1,
-// one DPP swap) the other half; the pair splits the 16 row-block scale
-// computations between them and swaps the results.  Down a column the thread
-// holds a whole block.  Each row of the tile writes a complete 128-byte line
-// of codes, each column 64 bytes.  One tile per workgroup: several resident
-// workgroups per CU keep HBM busy while others compute.  Loads are unconditional (edge
-// addresses are clamped into the tensor and the values zeroed at use), so
-// the compiler issues all 16 back to back.
+// Work decomposition.  A 256-thread workgroup owns a TR x 256 tile (TR = 32
+// or 64 rows).  Thread t loads 16-byte unit t % 32 (8 columns) of tile rows
+// t / 32 + 8k: a wave reads 2 rows x 512 bytes per load, all loads issued
+// back to back (edge addresses are clamped into the tensor; the duplicated
+// values never reach an output).
+//  - Row-wise pass, from registers: a 16-element row block spans a lane pair
+//    (lane ^ 1, one DPP swap); the pair splits the block-scale computations
+//    and swaps the results.  A wave writes 2 rows x 128 bytes of codes.
+//  - Transposed pass, through LDS: the bf16 tile is written once to an
+//    XOR-swizzled LDS buffer, and each lane reads one 4-byte column pair over
+//    a 16-row block (conflict-free), quantizing two column blocks.
+//  - Tile order: each XCD takes a contiguous range of an order that runs down
+//    bands of 256 rows column by column, so tiles sharing 128-byte lines of
+//    the transposed output meet in one L2.
 //
 // Arithmetic per block: the block amax is an integer max over bf16
-// magnitudes (packed 16-bit max; a NaN sorts above +Inf); s_raw = amax / (6 ts)
-// and r = 1 / (ts * s_b) use the refined division / reciprocal of formats.hpp
-// (equal to IEEE division in their guarded range); when s_raw falls in
-// UE5M3's normal range the encode is one rounding add on the fp32 bits, and
-// everything else (flushed, subnormal, saturated, NaN, out-of-range scales)
-// takes the general path.  Round-to-nearest payloads come from
-// v_cvt_scalef32_pk_fp4_f32 with scale 1.0, which rounds an fp32 value to
-// E2M1 exactly as the nearest-even definition does (checked on gfx950 for all
-// 2^32 non-NaN inputs); a NaN never reaches it: blocks whose scale is NaN or
-// whose reciprocal overflows take the software path.
+// magnitudes (packed 16-bit max; a NaN sorts above +Inf).  s_raw = amax/(6 ts)
+// uses the refined division of formats.hpp (equal to IEEE division wherever
+// the code depends on it); the UE5M3 code comes from the bits of s_raw
+// without branches (normal, subnormal, saturated); r = 1/(ts * s_b) comes
+// from a 256-entry table each workgroup builds with IEEE division.
+// Round-to-nearest payloads come from v_cvt_scalef32_pk_fp4_f32 with scale
+// 1.0, which rounds an fp32 value to E2M1 exactly as the nearest-even
+// definition does (checked on gfx950 for all 2^32 non-NaN inputs).  Blocks
+// the fast path cannot take (NaN/Inf amax, extreme tensor scales) make the
+// thread redo its blocks by the definition.
 #include "formats.hpp"
 #include "kernels.hpp"
 
@@ -40,7 +43,21 @@ namespace ue5m3fp4 {
 
 namespace {
 
-constexpr int kTileRows = 64;
+// Tile shape: TR (32 or 64) rows x 256 columns per 256-thread workgroup.
+// Stochastic rounding and row-only calls use 32-row tiles (more resident
+// workgroups hide more of the Philox and load latency); round-to-nearest
+// calls with the transposed output use 64-row tiles (32-byte runs of
+// transposed codes per column instead of 16).
+template <int TR>
+struct Shape {
+    static constexpr int kTileRows = TR;
+    static constexpr int kRowsPerThread = TR / 8;        // tile rows t / 32 + 8k
+    static constexpr int kRowBlocks = TR / 16;           // 16-row blocks per column
+    static constexpr int kPairsPerWave = 64 / kRowBlocks;  // column pairs per wave and pass
+    static constexpr int kColPasses = 128 / (4 * kPairsPerWave);
+    static constexpr int kBand = 256 / TR;               // tiles sharing a transposed line
+    static_assert(TR == 32 || TR == 64, "tile height");
+};
 constexpr int kTileCols = 256;
 constexpr int kThreads = 256;
 constexpr int kLdsRowBytes = kTileCols * 2;  // one bf16 tile row
@@ -65,10 +82,13 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
 }
 
 // LDS position of 16-byte unit u (8 columns) of tile row `row`: the unit
-// index is XORed with bits 4..5 of the row, so the column pass (lanes over 4
-// row blocks x 16 column pairs) reads 64 distinct banks.
+// index is XORed with the row's 16-row block times 16 / kRowBlocks, so the
+// column pass (lanes over kRowBlocks row blocks x kPairsPerWave column pairs)
+// reads 64 distinct banks.
+template <int TR>
 __device__ __forceinline__ int lds_offset(int row, int u) {
-    return row * kLdsRowBytes + ((u ^ (((row >> 4) & 3) << 2)) << 4);
+    constexpr int kRowBlocks = Shape<TR>::kRowBlocks;
+    return row * kLdsRowBytes + ((u ^ (((row >> 4) & (kRowBlocks - 1)) * (16 / kRowBlocks))) << 4);
 }
 
 struct Ctx {
@@ -181,41 +201,48 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
 
 // Workgroup id -> tile origin.  Workgroups are dispatched round-robin over
 // the 8 XCDs, each with its own L2.  Each XCD takes a contiguous range of a
-// tile order that runs down bands of 4 tile rows, column by column: the 4
-// tiles of a band column share the 128-byte lines of the transposed output
-// (32 bytes each) and the 8 neighbouring band columns share the lines of the
+// tile order that runs down bands of kBand tile rows (256 rows), column by
+// column: the tiles of a band column share the 128-byte lines of the
+// transposed output and the 8 neighbouring band columns share the lines of the
 // row-wise scales, so their partial lines meet in one L2 while resident and
 // reach HBM as whole lines.
+template <int TR>
 __device__ __forceinline__ void tile_of(uint32_t tiles_r, uint32_t tiles_c, int64_t& R0, int64_t& C0) {
+    constexpr int kBand = Shape<TR>::kBand, kTileRows = TR;
     const uint32_t n = tiles_r * tiles_c;
     uint32_t j = blockIdx.x;
     const uint32_t per_xcd = n / 8;
     if (j < per_xcd * 8) j = (j % 8) * per_xcd + j / 8;  // the tail keeps its id
-    const uint32_t band = j / (4 * tiles_c);
-    const uint32_t rem = j - band * 4 * tiles_c;
-    const uint32_t h = min(4u, tiles_r - 4 * band);  // rows in this band
-    const uint32_t tc = rem / h, tr = 4 * band + (rem - tc * h);
+    const uint32_t band = j / (kBand * tiles_c);
+    const uint32_t rem = j - band * kBand * tiles_c;
+    const uint32_t h = min((uint32_t)kBand, tiles_r - kBand * band);  // rows in this band
+    const uint32_t tc = rem / h, tr = kBand * band + (rem - tc * h);
     R0 = (int64_t)tr * kTileRows;
     C0 = (int64_t)tc * kTileCols;
 }
 
-template <bool ROW, bool COL, bool SR, bool AMAX>
+template <int TR, bool ROW, bool COL, bool SR, bool AMAX>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ tensor_scale, uint64_t seed, uint32_t offset,
     uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
     uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
     float* __restrict__ amax_inout) {
+    using S = Shape<TR>;
+    constexpr int kTileRows = S::kTileRows, kRowsPerThread = S::kRowsPerThread,
+                  kRowBlocks = S::kRowBlocks, kPairsPerWave = S::kPairsPerWave,
+                  kColPasses = S::kColPasses;
     __shared__ __align__(16) uint8_t tile[COL ? kTileRows * kLdsRowBytes : 16];
     __shared__ float rlut[(ROW || COL) ? 256 : 1];
     const int t = threadIdx.x;
     int64_t R0, C0;
-    tile_of((uint32_t)((rows + kTileRows - 1) / kTileRows), (uint32_t)((cols + kTileCols - 1) / kTileCols),
+    tile_of<TR>((uint32_t)((rows + kTileRows - 1) / kTileRows), (uint32_t)((cols + kTileCols - 1) / kTileCols),
             R0, C0);
     const bool interior = R0 + kTileRows <= rows && C0 + kTileCols <= cols;
 
     // ---- loads: thread t owns 16-byte unit u = t % 32 (8 columns) of tile
-    // rows t / 32 + 8k, k = 0..7; a wave reads 2 rows x 512 bytes per load.
+    // rows t / 32 + 8k, k < kRowsPerThread; a wave reads 2 rows x 512 bytes
+    // per load.
     // Loads are unconditional: addresses outside the tensor are clamped to
     // its last row / last 8 columns.  The duplicated values never reach an
     // output (cols % 16 == 0, and rows % 16 == 0 when the transposed output
@@ -223,11 +250,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const int u = t & 31, rbase = t >> 5;
     const int64_t c0 = C0 + 8 * u;
     const bool col_ok = c0 < cols;
-    u32x4 w[8];
+    u32x4 w[kRowsPerThread];
     {
         const uint16_t* src = x + (col_ok ? c0 : cols - 8);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kRowsPerThread; ++k) {
             const int64_t r = min(R0 + rbase + 8 * k, rows - 1);
             w[k] = *reinterpret_cast<const u32x4*>(src + r * ld);
         }
@@ -244,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
 
     // ---- row half-block amax (bf16 magnitude bits; NaN sorts above Inf)
-    uint32_t hmax[8];
+    uint32_t hmax[kRowsPerThread];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kRowsPerThread; ++k) {
         const uint32_t m = pk_max_u16(pk_max_u16(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu),
                                       pk_max_u16(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu));
         hmax[k] = max(m & 0xFFFFu, m >> 16);
@@ -254,13 +281,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint32_t tmax = 0u;
     if (AMAX) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) tmax = max(tmax, hmax[k]);
+        for (int k = 0; k < kRowsPerThread; ++k) tmax = max(tmax, hmax[k]);
     }
 
     if (COL) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<u32x4*>(tile + lds_offset(rbase + 8 * k, u)) = w[k];
+        for (int k = 0; k < kRowsPerThread; ++k)
+            *reinterpret_cast<u32x4*>(tile + lds_offset<TR>(rbase + 8 * k, u)) = w[k];
     }
     if (ROW || COL) __syncthreads();  // reciprocal table (and tile) visible
 
@@ -269,11 +296,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     // them.
     if (ROW) {
         const uint32_t p = t & 1;
-        uint32_t code[8];
-        float rr[8];
+        uint32_t code[kRowsPerThread];
+        float rr[kRowsPerThread];
         bool ok = ctx.fastK;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < kRowsPerThread / 2; ++m) {
             const uint32_t mine = p ? hmax[2 * m + 1] : hmax[2 * m];
             const uint32_t other = p ? hmax[2 * m] : hmax[2 * m + 1];
             const BlockScale own = block_scale(max(mine, swap_pair(other)), ctx, rlut, ok);
@@ -288,10 +315,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         // every lane (a short-circuit && would skip it where ok is false)
         const uint32_t ok_bit = ok ? 1u : 0u;
         const bool pair_ok = (ok_bit & swap_pair(ok_bit)) != 0u;
-        uint32_t packed[8];
+        uint32_t packed[kRowsPerThread];
         if (__builtin_expect(pair_ok, 1)) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kRowsPerThread; ++k) {
                 float v[8];
                 unpack8(w[k], v);
 #pragma unroll
@@ -303,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kRowsPerThread; ++k) {
                 const uint32_t blk = max(hmax[k], swap_pair(hmax[k]));  // both lanes active here
                 const BlockScale b = block_scale_general(blk, ctx.ts, ctx.K);
                 U32x4 rnd;
@@ -319,13 +346,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         if (interior) {
             // both lanes of a pair store the block's scale byte (same value)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kRowsPerThread; ++k) {
                 *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
                 ps[k * sstep] = (uint8_t)code[k];
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kRowsPerThread; ++k) {
                 if (col_ok && R0 + rbase + 8 * k < rows) {
                     *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
                     if (p == 0) ps[k * sstep] = (uint8_t)code[k];
@@ -334,20 +361,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         }
     }
 
-    // ---- transposed output: lane (rb, cp) = (lane % 4, lane / 4) of wave w
-    // quantizes columns 2j, 2j + 1 (j = 16 s + cp, slot s = w + 4 pass) over
-    // tile rows 16 rb .. 16 rb + 15: one 16-block per column.  The 4 lanes of
-    // a column write its 64 tile rows as 32 contiguous bytes.
+    // ---- transposed output: lane (rb, cp) = (lane % kRowBlocks,
+    // lane / kRowBlocks) of wave w quantizes columns 2j, 2j + 1
+    // (j = kPairsPerWave (w + 4 pass) + cp) over tile rows 16 rb .. 16 rb + 15:
+    // one 16-block per column.  The kRowBlocks lanes of a column write its
+    // tile rows as kTileRows / 2 contiguous bytes.
     if (COL) {
         const int lane = t & 63, wv = t >> 6;
-        const int rb = lane & 3, cp = lane >> 2;
+        const int rb = lane % kRowBlocks, cp = lane / kRowBlocks;
         const int64_t r0 = R0 + 16 * rb;
 #pragma unroll 1
-        for (int pass = 0; pass < 2; ++pass) {
-            const int j = 16 * (wv + 4 * pass) + cp;  // column pair within the tile
+        for (int pass = 0; pass < kColPasses; ++pass) {
+            const int j = kPairsPerWave * (wv + 4 * pass) + cp;  // column pair within the tile
             const int64_t ca = C0 + 2 * j;
             uint32_t cw[16];
-            const uint8_t* src = tile + lds_offset(16 * rb, j >> 2) + 4 * (j & 3);
+            const uint8_t* src = tile + lds_offset<TR>(16 * rb, j >> 2) + 4 * (j & 3);
 #pragma unroll
             for (int i = 0; i < 16; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(src + i * kLdsRowBytes);
             uint32_t m2 = 0u;
@@ -425,8 +453,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
 template <bool ROW, bool COL, bool SR, bool AMAX>
 void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
-    const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + kTileRows - 1) / kTileRows);
-    hipLaunchKernelGGL((quantize_kernel<ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
+    constexpr int TR = (COL && !SR) ? 64 : 32;
+    const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + TR - 1) / TR);
+    hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
                        a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
                        a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
 }
