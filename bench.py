@@ -257,7 +257,8 @@ def main():
 def quantize_only(lib, torch):
     """The quantizer alone on the 8192 x 4096 heavy-tailed activation workload
     (Student-t x normal body, 16 outlier columns x100): row-wise only and
-    row-wise + transposed, round-to-nearest and stochastic, tensor amax on.
+    row-wise + transposed, round-to-nearest and stochastic, tensor amax on;
+    and the current-tensor-scaling variant (amax pass + scale + quantize).
     8 device copies of the input and 8 output sets rotate (about 840 MB) so
     every launch reads and writes HBM, not the 256 MB cache.  GB/s counts the
     algorithmic bytes: 2 per element read, 0.5625 per element per output."""
@@ -277,12 +278,20 @@ def quantize_only(lib, torch):
     iters = 40
     res = {"workload": f"activations {rows}x{cols} bf16 (heavy-tailed, outlier columns)",
            "peak": HBM_PEAK_GBS, "unit": "GB/s", "buffer_sets": sets}
-    for name, rnd, both in (("rne_row", lib.RNE, False), ("rne_row_col", lib.RNE, True),
-                            ("sr_row", lib.SR, False), ("sr_row_col", lib.SR, True)):
+    ts_cur = torch.ones(1, dtype=torch.float32, device="cuda")
+    for name, rnd, both, current in (("rne_row", lib.RNE, False, False),
+                                     ("rne_row_col", lib.RNE, True, False),
+                                     ("sr_row", lib.SR, False, False),
+                                     ("sr_row_col", lib.SR, True, False),
+                                     ("current_scaling_rne_row_col", lib.RNE, True, True)):
         def run(i):
             k = i % sets
-            lib.quantize_blockscale(xs[k], ts, rnd, sr_seed(2), i, row=outs[k][0],
-                                    col=outs[k][1] if both else None, amax=amax)
+            if current:
+                lib.quantize_current_scaling(xs[k], ts_cur, amax, rnd, sr_seed(2), i, row=outs[k][0],
+                                             col=outs[k][1] if both else None)
+            else:
+                lib.quantize_blockscale(xs[k], ts, rnd, sr_seed(2), i, row=outs[k][0],
+                                        col=outs[k][1] if both else None, amax=amax)
         for i in range(sets):
             run(i)
         torch.cuda.synchronize()
@@ -297,6 +306,12 @@ def quantize_only(lib, torch):
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us": round(us, 2), "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "bytes": nbytes}
+    # current-tensor scaling reads x twice (amax pass, then quantization):
+    # its GB/s above counts the periodic path's algorithmic bytes, so the
+    # ratio of times is the cost of the extra pass that periodic scaling saves
+    cur = res["current_scaling_rne_row_col"]
+    cur["extra_read_bytes"] = rows * cols * 2
+    cur["time_vs_periodic"] = round(cur["us"] / res["rne_row_col"]["us"], 3)
     return res
 
 

@@ -37,6 +37,9 @@ _SIGNATURES = {
     "ue5m3fp4_gemm_wgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_update_tensor_scale": [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_float,
                                      _c_void_p],
+    "ue5m3fp4_quantize_current_scaling": [_c_void_p, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                          ctypes.c_uint64, ctypes.c_uint32, _c_void_p, _c_void_p,
+                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
 }
 
 _lib = None
@@ -234,6 +237,35 @@ def gemm_wgrad(dy_col, x_col, dw, stream=None):
                                             out_f, _ptr(dw), _stream(stream))
     _check(st, "ue5m3fp4_gemm_wgrad")
     return dw
+
+
+def quantize_current_scaling(x, tensor_scale, amax, rounding=RNE, seed=0, offset=0, row=None,
+                             col=None, max_safe=MAX_SAFE_DEFAULT, stream=None):
+    """Current-tensor scaling: amax pass over x into `amax`, tensor_scale =
+    amax / (6 max_safe) (left as passed when the amax is 0 or not finite),
+    then the block quantization with it.  row / col as in
+    quantize_blockscale (at least one)."""
+    import torch
+
+    _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its columns")
+    _require(tensor_scale, (torch.float32,), "tensor_scale")
+    _require(amax, (torch.float32,), "amax")
+    rc = rs = cc = cs = None
+    if row is not None:
+        rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
+    if col is not None:
+        cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
+    rows, cols = x.shape
+    if rc is not None and (tuple(rc.shape) != (rows, cols // 2) or tuple(rs.shape) != (rows, cols // 16)):
+        raise ValueError("row output buffers have the wrong shape")
+    if cc is not None and (tuple(cc.shape) != (cols, rows // 2) or tuple(cs.shape) != (cols, rows // 16)):
+        raise ValueError("col output buffers have the wrong shape")
+    st = load_library().ue5m3fp4_quantize_current_scaling(
+        _ptr(x), rows, cols, x.stride(0), float(max_safe), int(rounding), int(seed), int(offset),
+        _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs), _ptr(tensor_scale), _ptr(amax), _stream(stream))
+    _check(st, "ue5m3fp4_quantize_current_scaling")
 
 
 def update_tensor_scale(amax_running, tensor_scale, step, period=1,

@@ -21,6 +21,32 @@ int launch_status() {
     return e == hipSuccess ? UE5M3FP4_OK : UE5M3FP4_EHIP;
 }
 
+int check_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                   const float* tensor_scale, int rounding, const uint8_t* row_codes,
+                   const uint8_t* row_scales, const uint8_t* col_codes, const uint8_t* col_scales,
+                   const float* amax_inout) {
+    if (rows < 0 || cols < 0 || ld < 0) return UE5M3FP4_EINVAL;
+    if (rounding != UE5M3FP4_RNE && rounding != UE5M3FP4_SR) return UE5M3FP4_EINVAL;
+    if (cols % 16 != 0) return UE5M3FP4_ESHAPE;
+    if (rows >= kMaxDim || cols >= kMaxDim || rows * ld >= kMaxElems) return UE5M3FP4_ERANGE;
+    if (rows == 0 || cols == 0) return UE5M3FP4_OK;  // empty tensor: nothing to do
+    const bool row = row_codes || row_scales;
+    const bool col = col_codes || col_scales;
+    if (!x) return UE5M3FP4_EINVAL;
+    if ((row_codes == nullptr) != (row_scales == nullptr)) return UE5M3FP4_EINVAL;
+    if ((col_codes == nullptr) != (col_scales == nullptr)) return UE5M3FP4_EINVAL;
+    if (!row && !col && !amax_inout) return UE5M3FP4_EINVAL;  // nothing requested
+    if ((row || col) && !tensor_scale) return UE5M3FP4_EINVAL;
+    if (col && rows % 16 != 0) return UE5M3FP4_ESHAPE;
+    if (ld < cols) return UE5M3FP4_ESHAPE;
+    if (ld % 8 != 0 || !aligned16(x)) return UE5M3FP4_EALIGN;
+    if ((row && (!aligned16(row_codes) || !aligned16(row_scales))) ||
+        (col && (!aligned16(col_codes) || !aligned16(col_scales))) ||
+        (tensor_scale && !aligned4(tensor_scale)) || (amax_inout && !aligned4(amax_inout)))
+        return UE5M3FP4_EALIGN;
+    return UE5M3FP4_OK;
+}
+
 int check_gemm(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_t* bc,
                const uint8_t* bs, const float* bt, int64_t M, int64_t N, int64_t K,
                const float* c) {
@@ -57,29 +83,39 @@ int ue5m3fp4_quantize_blockscale(const uint16_t* x, int64_t rows, int64_t cols, 
                                  uint32_t offset, uint8_t* row_codes, uint8_t* row_scales,
                                  uint8_t* col_codes, uint8_t* col_scales, float* amax_inout,
                                  void* stream) {
-    if (rows < 0 || cols < 0 || ld < 0) return UE5M3FP4_EINVAL;
-    if (rounding != UE5M3FP4_RNE && rounding != UE5M3FP4_SR) return UE5M3FP4_EINVAL;
-    if (cols % 16 != 0) return UE5M3FP4_ESHAPE;
-    if (rows >= kMaxDim || cols >= kMaxDim || rows * ld >= kMaxElems) return UE5M3FP4_ERANGE;
-    if (rows == 0 || cols == 0) return UE5M3FP4_OK;  // empty tensor: nothing to do
-    const bool row = row_codes || row_scales;
-    const bool col = col_codes || col_scales;
-    if (!x) return UE5M3FP4_EINVAL;
-    if ((row_codes == nullptr) != (row_scales == nullptr)) return UE5M3FP4_EINVAL;
-    if ((col_codes == nullptr) != (col_scales == nullptr)) return UE5M3FP4_EINVAL;
-    if (!row && !col && !amax_inout) return UE5M3FP4_EINVAL;  // nothing requested
-    if ((row || col) && !tensor_scale) return UE5M3FP4_EINVAL;
-    if (col && rows % 16 != 0) return UE5M3FP4_ESHAPE;
-    if (ld < cols) return UE5M3FP4_ESHAPE;
-    if (ld % 8 != 0 || !aligned16(x)) return UE5M3FP4_EALIGN;
-    if ((row && (!aligned16(row_codes) || !aligned16(row_scales))) ||
-        (col && (!aligned16(col_codes) || !aligned16(col_scales))) ||
-        (tensor_scale && !aligned4(tensor_scale)) || (amax_inout && !aligned4(amax_inout)))
-        return UE5M3FP4_EALIGN;
+    const int st = check_quantize(x, rows, cols, ld, tensor_scale, rounding, row_codes, row_scales,
+                                  col_codes, col_scales, amax_inout);
+    if (st != UE5M3FP4_OK || rows == 0 || cols == 0) return st;
     QuantizeArgs a{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
                    seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
                    amax_inout};
     launch_quantize_blockscale(a, (hipStream_t)stream);
+    return launch_status();
+}
+
+int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                      float max_safe, int rounding, uint64_t seed, uint32_t offset,
+                                      uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                                      uint8_t* col_scales, float* tensor_scale, float* amax_out,
+                                      void* stream) {
+    if (!tensor_scale || !amax_out) return UE5M3FP4_EINVAL;
+    if (!(max_safe > 0.0f) || !std::isfinite(max_safe)) return UE5M3FP4_EINVAL;
+    if (!row_codes && !col_codes) return UE5M3FP4_EINVAL;  // no output requested
+    const int st = check_quantize(x, rows, cols, ld, tensor_scale, rounding, row_codes, row_scales,
+                                  col_codes, col_scales, amax_out);
+    if (st != UE5M3FP4_OK || rows == 0 || cols == 0) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    // 1. amax pass over x
+    launch_zero_scalar(amax_out, s);
+    QuantizeArgs pre{x, rows, cols, ld, nullptr, false, 0, 0, nullptr, nullptr, nullptr, nullptr, amax_out};
+    launch_quantize_blockscale(pre, s);
+    // 2. the tensor scale of this tensor
+    launch_current_tensor_scale(amax_out, tensor_scale, max_safe, s);
+    // 3. block quantization with it (the amax is already known)
+    QuantizeArgs q{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
+                   seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
+                   nullptr};
+    launch_quantize_blockscale(q, s);
     return launch_status();
 }
 

@@ -29,6 +29,12 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float*
 void launch_update_tensor_scale(float* amax_running, float* tensor_scale, float max_safe,
                                 hipStream_t stream);
 
+// Current-tensor scaling: *amax = 0 (before an amax pass) and
+// *tensor_scale = amax / (6 max_safe) when finite and > 0 (amax kept).
+void launch_zero_scalar(float* p, hipStream_t stream);
+void launch_current_tensor_scale(const float* amax, float* tensor_scale, float max_safe,
+                                 hipStream_t stream);
+
 struct GemmArgs {
     const uint8_t* a_codes;
     const uint8_t* a_scales;

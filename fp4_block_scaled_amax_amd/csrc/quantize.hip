@@ -221,6 +221,64 @@ __device__ __forceinline__ void tile_of(uint32_t tiles_r, uint32_t tiles_c, int6
     C0 = (int64_t)tc * kTileCols;
 }
 
+// Tensor amax of a workgroup (bf16 magnitude bits of each thread's max)
+// folded into *amax (fp32 bits; a non-negative float orders as its bits, and
+// a NaN's bits above +Inf).  Wave reduction, then the workgroup's waves meet
+// in LDS and one lane issues the atomic -- only when the workgroup's max
+// exceeds the (possibly stale) running value: same-address atomics
+// serialize across the XCDs, and a max only grows, so skipping is exact.
+__device__ __forceinline__ void amax_commit(uint32_t tmax, float* amax) {
+    __shared__ uint32_t wave_max[16];
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 32));
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 16));
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 8));
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 4));
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 2));
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, 1));
+    const int wv = threadIdx.x >> 6, waves = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) wave_max[wv] = tmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0u;
+        for (int i = 0; i < waves; ++i) m = max(m, wave_max[i]);
+        if (m != 0u) {
+            unsigned int* dst = reinterpret_cast<unsigned int*>(amax);
+            const unsigned int seen = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((m << 16) > seen) atomicMax(dst, m << 16);
+        }
+    }
+}
+
+// Amax-only pass (the bootstrap before the first refresh, and the first step
+// of current-tensor scaling): a grid-stride max over |x| with 16-byte loads,
+// four in flight per thread, one atomic per workgroup.
+__global__ __launch_bounds__(1024) void amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld,
+                                                    float* __restrict__ amax) {
+    const int64_t units_row = cols / 8;  // 16-byte units per row (cols % 16 == 0)
+    const int64_t units = rows * units_row;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t m = 0u;
+    auto unit_max = [&](int64_t i) __attribute__((always_inline)) {
+        const int64_t r = ld == cols ? 0 : i / units_row;
+        const int64_t off = ld == cols ? i * 8 : r * ld + (i - r * units_row) * 8;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(x + off);
+        const uint32_t p = pk_max_u16(pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                                      pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+        return p;
+    };
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t p2 = 0u;
+    for (; i + 3 * stride < units; i += 4 * stride) {
+        const uint32_t a = unit_max(i), b = unit_max(i + stride);
+        const uint32_t c = unit_max(i + 2 * stride), d = unit_max(i + 3 * stride);
+        p2 = pk_max_u16(p2, pk_max_u16(pk_max_u16(a, b), pk_max_u16(c, d)));
+    }
+    for (; i < units; i += stride) p2 = pk_max_u16(p2, unit_max(i));
+    m = max(p2 & 0xFFFFu, p2 >> 16);
+    amax_commit(m, amax);
+}
+
 template <int TR, bool ROW, bool COL, bool SR, bool AMAX>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -435,20 +493,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         }
     }
 
-    // ---- tensor amax: wave reduction; the atomic is issued only when the
-    // wave's max exceeds the running value already there.  Atomics on one
-    // address from every wave serialize across the XCDs; a max only grows,
-    // so skipping when the (possibly stale) value read is already >= ours is
-    // exact.
-    if (AMAX) {
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, s));
-        if ((t & 63) == 0 && tmax != 0u) {
-            unsigned int* dst = reinterpret_cast<unsigned int*>(amax_inout);
-            const unsigned int seen = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((tmax << 16) > seen) atomicMax(dst, tmax << 16);
-        }
-    }
+    // ---- tensor amax: one atomic per workgroup
+    if (AMAX) amax_commit(tmax, amax_inout);
 }
 
 template <bool ROW, bool COL, bool SR, bool AMAX>
@@ -458,6 +504,23 @@ void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
                        a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
                        a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
+}
+
+// Compute units of the current device (the runtime caches the attribute).
+int cu_count() {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+        return c;
+    return 256;
+}
+
+void launch_amax(const QuantizeArgs& a, hipStream_t s) {
+    const int64_t units = a.rows * (a.cols / 8);
+    const int64_t want = (units + 4 * 1024 - 1) / (4 * 1024);
+    const int64_t grid = max((int64_t)1, min(want, (int64_t)cu_count() * 2));
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(1024), 0, s, a.x, a.rows, a.cols, a.ld,
+                       a.amax_inout);
 }
 
 template <bool ROW, bool COL, bool SR>
@@ -520,7 +583,31 @@ __global__ void update_tensor_scale_kernel(float* __restrict__ amax_running,
     *amax_running = 0.0f;
 }
 
+__global__ void zero_scalar_kernel(float* __restrict__ p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
+}
+
+// ts = amax / (6 max_safe) from the current tensor's amax, which is kept;
+// a zero or non-finite amax leaves ts unchanged.
+__global__ void current_tensor_scale_kernel(const float* __restrict__ amax,
+                                            float* __restrict__ tensor_scale, float max_safe) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const float a = *amax;
+    const uint32_t b = __float_as_uint(a);
+    if ((b & 0x7F800000u) != 0x7F800000u && a > 0.0f) *tensor_scale = a / (6.0f * max_safe);
+}
+
 }  // namespace
+
+void launch_zero_scalar(float* p, hipStream_t s) {
+    hipLaunchKernelGGL(zero_scalar_kernel, dim3(1), dim3(64), 0, s, p);
+}
+
+void launch_current_tensor_scale(const float* amax, float* tensor_scale, float max_safe,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(current_tensor_scale_kernel, dim3(1), dim3(64), 0, s, amax, tensor_scale,
+                       max_safe);
+}
 
 void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t s) {
     const bool row = a.row_codes != nullptr;
@@ -528,7 +615,7 @@ void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t s) {
     if (row && col) dispatch_sr<true, true>(a, s);
     else if (row) dispatch_sr<true, false>(a, s);
     else if (col) dispatch_sr<false, true>(a, s);
-    else launch_quantize<false, false, false, true>(a, s);  // amax-only pass
+    else launch_amax(a, s);  // amax-only pass
 }
 
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,

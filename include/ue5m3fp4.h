@@ -110,6 +110,25 @@ UE5M3FP4_API int ue5m3fp4_quantize_blockscale(const uint16_t* x, int64_t rows, i
                                  uint8_t* col_codes, uint8_t* col_scales, float* amax_inout,
                                  void* stream);
 
+/* Current-tensor scaling, the alternative to the periodic refresh: the
+ * tensor scale comes from this tensor's own amax, which costs one more read
+ * of x (UE5M3 paper, abstract: the UE5M3 range is what lets the recipe use
+ * periodic instead of current tensor scaling; this call measures what that
+ * saves).  Three steps on `stream`:
+ *   1. *amax_out = max|x| (an amax pass; a NaN in x propagates);
+ *   2. *tensor_scale = fp32(*amax_out / fp32(6 * max_safe)) when *amax_out
+ *      is finite and > 0, else *tensor_scale is left as passed;
+ *   3. the block quantization of ue5m3fp4_quantize_blockscale with that
+ *      tensor scale (same outputs, layouts, rounding and random stream).
+ * At least one output pair is required; tensor_scale and amax_out are device
+ * fp32 scalars (tensor_scale is read only in the fallback of step 2).
+ * max_safe > 0 and finite.  Other rules as ue5m3fp4_quantize_blockscale. */
+UE5M3FP4_API int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                      float max_safe, int rounding, uint64_t seed, uint32_t offset,
+                                      uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                                      uint8_t* col_scales, float* tensor_scale, float* amax_out,
+                                      void* stream);
+
 /* out[i][j] = fp32(fp32(e2m1 * ue5m3) * ts) for a quantized rows x cols
  * operand (the product q * s_b is exact, so there is one rounding).  Blocks
  * with scale 0xFF give NaN.  out is fp32 [rows][cols].  cols % 16 == 0. */

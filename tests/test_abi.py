@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -72,6 +72,26 @@ def test_quantize_argument_checks(L):
     # empty tensors are valid no-ops and touch nothing (even NULL pointers)
     assert q(L, rows=0, x=None, rc=None, rs=None, cc=None, cs=None) == OK
     assert q(L, cols=0, ld=0, x=None) == OK
+
+
+def qc(L, x=P, rows=32, cols=32, ld=32, ms=7168.0, rnd=0, rc=P, rs=P, cc=P, cs=P, ts=P, amax=P):
+    return L.ue5m3fp4_quantize_current_scaling(x, rows, cols, ld, ms, rnd, 0, 0, rc, rs, cc, cs, ts,
+                                               amax, None)
+
+
+def test_current_scaling_argument_checks(L):
+    assert qc(L, ts=None) == EINVAL
+    assert qc(L, amax=None) == EINVAL
+    assert qc(L, ms=0.0) == EINVAL
+    assert qc(L, ms=float("inf")) == EINVAL
+    assert qc(L, ms=float("nan")) == EINVAL
+    assert qc(L, rc=None, rs=None, cc=None, cs=None) == EINVAL  # an amax pass alone is not this call
+    assert qc(L, rnd=3) == EINVAL
+    assert qc(L, cols=40, ld=40) == ESHAPE
+    assert qc(L, rows=40) == ESHAPE
+    assert qc(L, amax=P + 2) == EALIGN
+    assert qc(L, x=P + 8) == EALIGN
+    assert qc(L, rows=0, x=None) == OK  # empty tensor: nothing launched
 
 
 def test_gemm_argument_checks(L):

@@ -220,3 +220,27 @@ def test_update_tensor_scale(cuda_device):
     a_dev, t_dev = dev_scalar(3.0), dev_scalar(1.0)
     lib.update_tensor_scale(a_dev, t_dev, 0, 1, max_safe=0.5)
     assert host(t_dev)[0] == np.float32(1.0)
+
+
+@pytest.mark.parametrize("rounding,name", MODES)
+@pytest.mark.parametrize("shape,kind", [((272, 528), "heavy"), ((1024, 1040), "logrange"),
+                                        ((64, 256), "zeros")])
+def test_current_scaling(cuda_device, rounding, name, shape, kind):
+    """Current-tensor scaling: the amax of this tensor, ts = amax / (6 max_safe)
+    (the update rule applied to a fresh amax, ts kept when the amax is 0),
+    then the same block quantization -- codes, scales, amax and ts bit-exact."""
+    if kind == "zeros":
+        bits = np.zeros(shape, dtype=np.uint16)
+    else:
+        bits = random_bf16(shape, seed=7 + shape[0], kind=kind)
+    amax_ref = quantize.tensor_amax(bits)
+    _, ts_ref = tensor_scale.update_tensor_scale(amax_ref, np.float32(0.5), 0, 1)
+    x = dev_bf16(bits)
+    ts_dev, amax_dev = dev_scalar(0.5), dev_scalar(123.0)
+    rows, cols = shape
+    qr, qc = lib.empty_quantized(rows, cols, ts_dev), lib.empty_quantized(cols, rows, ts_dev)
+    lib.quantize_current_scaling(x, ts_dev, amax_dev, rounding, seed=5, offset=9, row=qr, col=qc)
+    assert host(amax_dev)[0] == amax_ref
+    assert host(ts_dev)[0] == ts_ref
+    assert_quant_equal(qr, bits, ts_ref, rounding, 5, 9, 0)
+    assert_quant_equal(qc, bits, ts_ref, rounding, 5, 9, 1)
