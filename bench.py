@@ -20,6 +20,8 @@ command, reported only while the GEMM source still matches the one profiled.
 and stochastic calls separately) and, as `quantize_activations`, on its own
 over the 8192 x 4096 heavy-tailed activation workload with 8 rotating
 HBM-resident buffer sets (the quantizer's bandwidth roofline).
+`epilogue_fusion` times the largest fprop of the step with its output fused
+for the next layer (bf16 Y and its amax) against the fp32 output.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 `--copy-calibration` instead runs a plain 256 MiB device copy, whose
@@ -245,6 +247,7 @@ def main():
                      "rne": q_stats(lib.RNE), "sr": q_stats(lib.SR)},
     }
     step_elems = sum(t.elems for t in tensors)
+    result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
     del layers, tensors
     torch.cuda.empty_cache()
     if not args.no_quantize_only:
@@ -252,6 +255,34 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step_flops, step_elems)
     print(json.dumps(result), flush=True)
+
+
+def epilogue_fusion(lib, torch, up):
+    """The up projection's fprop (8192 x 16384 x 4096, the largest output of
+    the step) with its output fused for the next layer -- bf16 Y plus its
+    tensor amax -- against the fp32 output, on the same quantized operands."""
+    X, W = up[0], up[1]
+    tokens, out_f = X.row.rows, W.row.rows
+    y32 = torch.empty((tokens, out_f), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((tokens, out_f), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    flop = 2.0 * tokens * out_f * X.row.cols
+    res = {"shape": f"{tokens}x{out_f}x{X.row.cols}"}
+    for name, fn in (("fp32_out", lambda: lib.gemm_fprop(X.row, W.row, y32)),
+                     ("bf16_out_amax", lambda: lib.gemm_nt_bf16(X.row, W.row, y16, amax=amax))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        res[name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "output_bytes": tokens * out_f * (4 if name == "fp32_out" else 2)}
+    return res
 
 
 def quantize_only(lib, torch):

@@ -32,6 +32,7 @@ _SIGNATURES = {
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "ue5m3fp4_dequantize": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_nt_bf16": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_fprop": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_dgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_wgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
@@ -192,6 +193,25 @@ def gemm_nt(a, b, out, stream=None):
                                          _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
                                          b.rows, a.cols, _ptr(out), _stream(stream))
     _check(st, "ue5m3fp4_gemm_nt")
+    return out
+
+
+def gemm_nt_bf16(a, b, out, amax=None, stream=None):
+    """out[M][N] (bf16) = bf16(tsA * tsB * A B^T), round to nearest even;
+    amax (device fp32 scalar or None) receives max(amax, max|out|)."""
+    import torch
+
+    if a.cols != b.cols:
+        raise ValueError("A and B disagree on K")
+    _require(out, (torch.bfloat16, torch.int16, torch.uint16), "out", 2)
+    if tuple(out.shape) != (a.rows, b.rows) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous ({a.rows}, {b.rows}) tensor")
+    if amax is not None:
+        _require(amax, (torch.float32,), "amax")
+    st = load_library().ue5m3fp4_gemm_nt_bf16(_ptr(a.codes), _ptr(a.scales), _ptr(a.ts),
+                                              _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
+                                              b.rows, a.cols, _ptr(out), _ptr(amax), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_nt_bf16")
     return out
 
 

@@ -49,7 +49,7 @@ int check_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
 
 int check_gemm(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_t* bc,
                const uint8_t* bs, const float* bt, int64_t M, int64_t N, int64_t K,
-               const float* c) {
+               const void* c) {
     if (M < 0 || N < 0 || K < 0) return UE5M3FP4_EINVAL;
     if (K % 16 != 0) return UE5M3FP4_ESHAPE;
     if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return UE5M3FP4_ERANGE;
@@ -69,7 +69,19 @@ int run_gemm(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_
     const int st = check_gemm(ac, as, at, bc, bs, bt, M, N, K, c);
     if (st != UE5M3FP4_OK) return st;
     if (M == 0 || N == 0) return UE5M3FP4_OK;
-    GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, c};
+    GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, c, nullptr, nullptr};
+    launch_gemm_nt(g, (hipStream_t)stream);
+    return launch_status();
+}
+
+int run_gemm_bf16(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_t* bc,
+                  const uint8_t* bs, const float* bt, int64_t M, int64_t N, int64_t K, uint16_t* c,
+                  float* amax, void* stream) {
+    const int st = check_gemm(ac, as, at, bc, bs, bt, M, N, K, c);
+    if (st != UE5M3FP4_OK) return st;
+    if (amax && !aligned4(amax)) return UE5M3FP4_EALIGN;
+    if (M == 0 || N == 0) return UE5M3FP4_OK;
+    GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, nullptr, c, amax};
     launch_gemm_nt(g, (hipStream_t)stream);
     return launch_status();
 }
@@ -136,6 +148,14 @@ int ue5m3fp4_gemm_nt(const uint8_t* a_codes, const uint8_t* a_scales, const floa
                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
                      int64_t M, int64_t N, int64_t K, float* c, void* stream) {
     return run_gemm(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, stream);
+}
+
+int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                          const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                          int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
+                          void* stream) {
+    return run_gemm_bf16(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, amax_inout,
+                         stream);
 }
 
 int ue5m3fp4_gemm_fprop(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_ts,

@@ -164,12 +164,46 @@ struct Frags {
     f16x8_t a[4], b[4];
 };
 
-template <bool ALIGNED>
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    const __bf16 b = (__bf16)f;
+    uint16_t u;
+    __builtin_memcpy(&u, &b, 2);
+    return u;
+}
+
+// max of |bf16| bits over the workgroup folded into *amax (fp32 bits of a
+// non-negative float order as integers; NaN above +Inf): wave and LDS
+// reduction, one atomic per workgroup, skipped when the running value is
+// already at least as large.
+__device__ __forceinline__ void amax_commit(uint32_t m, float* amax) {
+    __shared__ uint32_t wave_max[kThreads / 64];
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int i = 0; i < kThreads / 64; ++i) w = max(w, wave_max[i]);
+        if (w != 0u) {
+            unsigned int* dst = reinterpret_cast<unsigned int*>(amax);
+            const unsigned int seen = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((w << 16) > seen) atomicMax(dst, w << 16);
+        }
+    }
+}
+
+template <bool ALIGNED, bool BF16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, const float* __restrict__ b_ts, int64_t M, int64_t N,
-    int64_t K, float* __restrict__ C) {
+    int64_t K, float* __restrict__ C, uint16_t* __restrict__ Cb, float* __restrict__ amax) {
     __shared__ __align__(16) uint8_t smem[kSmem];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem + kLut);
 
@@ -341,21 +375,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
         }
     }
 
-    // ---- epilogue: C = (acc * 256 tsA) * tsB.  Accumulator register e of lane
-    // (r, h) holds row 8 * (e / 4) + 4 * h + e % 4, column r of a 32 x 32 tile.
+    // ---- epilogue: C = (acc * 256 tsA) * tsB, stored as fp32, or rounded to
+    // bf16 with the tensor amax of the stored values folded into *amax.
+    // Accumulator register e of lane (r, h) holds row 8 * (e / 4) + 4 * h +
+    // e % 4, column r of a 32 x 32 tile.
     const float sa256 = *a_ts * 256.0f, tsb = *b_ts;
     const int64_t row0 = m0 + wm * 128 + 4 * h, col0 = n0 + wn * 128 + r;
+    uint32_t tmax = 0u;  // max |bf16| bits stored by this lane
     if (m0 + kBM <= M && n0 + kBN <= N) {
         // interior tile: one row pointer per accumulator row, the 4 column
         // tiles at immediate offsets
-        float* base = C + row0 * N + col0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float* rowp = base + (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * N;
+                const int64_t off = (row0 + i * 32 + 8 * (e >> 2) + (e & 3)) * N + col0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) rowp[j * 32] = (acc[i][j][e] * sa256) * tsb;
+                for (int j = 0; j < 4; ++j) {
+                    const float v = (acc[i][j][e] * sa256) * tsb;
+                    if (BF16) {
+                        const uint16_t b = to_bf16(v);
+                        Cb[off + j * 32] = b;
+                        tmax = max(tmax, (uint32_t)(b & 0x7FFFu));
+                    } else {
+                        C[off + j * 32] = v;
+                    }
+                }
             }
     } else {
 #pragma unroll
@@ -366,23 +411,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int64_t row = row0 + i * 32 + 8 * (e >> 2) + (e & 3);
-                    if (row < M && col < N) C[row * N + col] = (acc[i][j][e] * sa256) * tsb;
+                    if (row < M && col < N) {
+                        const float v = (acc[i][j][e] * sa256) * tsb;
+                        if (BF16) {
+                            const uint16_t b = to_bf16(v);
+                            Cb[row * N + col] = b;
+                            tmax = max(tmax, (uint32_t)(b & 0x7FFFu));
+                        } else {
+                            C[row * N + col] = v;
+                        }
+                    }
                 }
             }
     }
+    if (BF16 && amax != nullptr) amax_commit(tmax, amax);
 }
 
 }  // namespace
 
-void launch_gemm_nt(const GemmArgs& g, hipStream_t stream) {
+template <bool ALIGNED, bool BF16>
+void launch_gemm(const GemmArgs& g, hipStream_t stream) {
     const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)tiles);
-    if (g.K % kBK == 0) {
-        hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kThreads), 0, stream, g.a_codes,
-                           g.a_scales, g.a_ts, g.b_codes, g.b_scales, g.b_ts, g.M, g.N, g.K, g.c);
+    hipLaunchKernelGGL((gemm_nt_kernel<ALIGNED, BF16>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+                       g.a_codes, g.a_scales, g.a_ts, g.b_codes, g.b_scales, g.b_ts, g.M, g.N, g.K, g.c,
+                       g.c_bf16, g.amax);
+}
+
+void launch_gemm_nt(const GemmArgs& g, hipStream_t stream) {
+    const bool aligned = g.K % kBK == 0;
+    if (g.c_bf16) {
+        if (aligned) launch_gemm<true, true>(g, stream);
+        else launch_gemm<false, true>(g, stream);
     } else {
-        hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kThreads), 0, stream, g.a_codes,
-                           g.a_scales, g.a_ts, g.b_codes, g.b_scales, g.b_ts, g.M, g.N, g.K, g.c);
+        if (aligned) launch_gemm<true, false>(g, stream);
+        else launch_gemm<false, false>(g, stream);
     }
 }
 

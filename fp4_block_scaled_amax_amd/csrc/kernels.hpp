@@ -43,7 +43,9 @@ struct GemmArgs {
     const uint8_t* b_scales;
     const float* b_ts;
     int64_t M, N, K;
-    float* c;
+    float* c;             // fp32 output, or
+    uint16_t* c_bf16;     // bf16 output (round to nearest even) ...
+    float* amax;          // ... with max|C_bf16| folded into *amax (nullable)
 };
 
 void launch_gemm_nt(const GemmArgs& g, hipStream_t stream);

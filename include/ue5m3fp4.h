@@ -143,6 +143,21 @@ UE5M3FP4_API int ue5m3fp4_gemm_nt(const uint8_t* a_codes, const uint8_t* a_scale
                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
                      int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
+/* ue5m3fp4_gemm_nt with its output fused for the next linear layer:
+ * C = (tsA * tsB) * sum_k A(i,k) B(j,k) computed as in ue5m3fp4_gemm_nt,
+ * then rounded to bf16 (round to nearest even; NaN stays NaN) and stored as
+ * bf16 [M][N] (row stride N); when amax_inout is non-NULL, max |C_bf16| over
+ * the stored values is folded into *amax_inout (the running amax the next
+ * quantization's tensor scale is refreshed from; a NaN propagates).
+ * Format-aware fusion article (similar-articles list of the UFP4 page):
+ * fusing the steps around the FP4 GEMM is where the throughput is.  c must
+ * be 16-byte aligned, amax_inout 4-byte aligned.  Other rules as
+ * ue5m3fp4_gemm_nt. */
+UE5M3FP4_API int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                          const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                          int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
+                          void* stream);
+
 /* fprop: Y = X W^T.  UFP4 paper, abstract (three training GEMMs).
  *   x: X [tokens][in] quantized row-wise (codes [tokens][in/2]);
  *   w: W [out][in] quantized row-wise (codes [out][in/2]);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -113,6 +113,16 @@ def test_gemm_argument_checks(L):
         fn = getattr(L, name)
         assert fn(P, P, P, P, P, P, *dims, P, None) == ESHAPE
         assert fn(P, P, P, P, P, P, 0, 0, 0, None, None) == OK
+
+
+def test_gemm_bf16_argument_checks(L):
+    g = L.ue5m3fp4_gemm_nt_bf16
+    assert g(P, P, P, P, P, P, 4, 4, 24, P, None, None) == ESHAPE       # K % 16
+    assert g(P, P, P, P, P, P, 4, 4, 16, None, None, None) == EINVAL     # no output
+    assert g(P, P, P, P, P, P, 4, 4, 16, P + 2, None, None) == EALIGN
+    assert g(P, P, P, P, P, P, 4, 4, 16, P, P + 2, None) == EALIGN       # amax alignment
+    assert g(P, P, P, P, P, P, 1 << 31, 4, 16, P, None, None) == ERANGE
+    assert g(None, None, None, None, None, None, 4, 0, 16, None, None, None) == OK  # empty
 
 
 def test_fprop_dgrad_wgrad_contract_the_right_axis(L):

@@ -209,3 +209,67 @@ def test_dequant_exhaustive_through_gemm(cuda_device):
         assert np.array_equal(got[~nan], ref[~nan]), (pos, np.argwhere(got[~nan] != ref[~nan])[:4])
         rest = host(c)[:, 1:]  # B rows of zeros: 0, or NaN where A's block scale is NaN
         assert np.all(rest[~nan] == 0) and np.all(np.isnan(rest[nan]))
+
+
+def _fp32_down(x):
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) > x, np.nextafter(f, np.float32(-np.inf)), f)
+
+
+def _fp32_up(x):
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) < x, np.nextafter(f, np.float32(np.inf)), f)
+
+
+def _bf16_rne(f32):
+    """fp32 -> bf16 value (round to nearest even) by torch's CPU cast."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(f32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (300, 200, 4112), (33, 130, 48), (1, 1, 16)])
+def test_gemm_nt_bf16_with_amax(cuda_device, M, N, K):
+    """Fused epilogue: bf16 output and its amax.  Each bf16 value must be the
+    round-to-nearest-even image of some fp32 within the GEMM tolerance of the
+    oracle (rounding is monotone, so it lies between the images of the ends of
+    that interval); the amax must be the max |.| of the values stored."""
+    import torch
+
+    rng = np.random.default_rng(M + 5 * N + 11 * K)
+    a, ac, asc = _random_operand(rng, M, K, 0x40, 0xB0, ts=0.5)
+    b, bc, bsc = _random_operand(rng, N, K, 0x40, 0xB0, ts=2.0e-3)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    amax = dev_scalar(0.0)
+    lib.gemm_nt_bf16(a, b, out, amax=amax)
+    got = out.to(torch.float32).cpu().numpy().astype(np.float64)
+    from oracle import gemm as ogemm
+
+    ref, bound = ogemm.gemm_nt(ac, asc, 0.5, bc, bsc, 2.0e-3)
+    tol = 1e-5 * bound
+    lo = _bf16_rne(_fp32_down(ref - tol)).astype(np.float64)
+    hi = _bf16_rne(_fp32_up(ref + tol)).astype(np.float64)
+    bad = np.argwhere((got < lo) | (got > hi))
+    assert bad.size == 0, f"bf16 output outside the rounded tolerance band at {bad[:3].tolist()}"
+    assert host(amax)[0] == np.float32(np.max(np.abs(got)))
+    # a larger running amax is left alone
+    big = dev_scalar(1e30)
+    lib.gemm_nt_bf16(a, b, out, amax=big)
+    assert host(big)[0] == np.float32(1e30)
+
+
+def test_gemm_nt_bf16_nan_block(cuda_device):
+    """A NaN block scale (0xFF) poisons its output row in bf16 and the amax."""
+    import torch
+
+    rng = np.random.default_rng(3)
+    a, ac, asc = _random_operand(rng, 40, 64, 0x40, 0xB0)
+    b, bc, bsc = _random_operand(rng, 24, 64, 0x40, 0xB0)
+    asc[7, 2] = 0xFF
+    a = lib.Quantized(a.codes, torch.from_numpy(asc).cuda(), a.ts)
+    out = torch.empty((40, 24), dtype=torch.bfloat16, device="cuda")
+    amax = dev_scalar(0.0)
+    lib.gemm_nt_bf16(a, b, out, amax=amax)
+    got = out.to(torch.float32).cpu().numpy()
+    assert np.all(np.isnan(got[7])) and not np.any(np.isnan(np.delete(got, 7, axis=0)))
+    assert np.isnan(host(amax)[0])

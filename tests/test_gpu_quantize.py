@@ -244,3 +244,33 @@ def test_current_scaling(cuda_device, rounding, name, shape, kind):
     assert host(ts_dev)[0] == ts_ref
     assert_quant_equal(qr, bits, ts_ref, rounding, 5, 9, 0)
     assert_quant_equal(qc, bits, ts_ref, rounding, 5, 9, 1)
+
+
+@pytest.mark.parametrize("shape,ld,kind", [((48, 64), 64, "heavy"), ((37, 80), 96, "normal"),
+                                           ((4096, 528), 528, "logrange"), ((3, 16), 24, "normal"),
+                                           ((2048, 4096), 4096, "gradient")])
+def test_amax_only_pass(cuda_device, shape, ld, kind):
+    """The amax-only pass (bootstrap and current scaling): contiguous and
+    strided rows, grid-stride tails, a running value that is already larger,
+    and NaN propagation."""
+    import torch
+
+    rows, cols = shape
+    bits = random_bf16(shape, seed=rows + ld, kind=kind)
+    full = np.zeros((rows, ld), dtype=np.uint16)
+    full[:, :cols] = bits
+    full[:, cols:] = 0x7F80  # +Inf in the padding must not be read
+    xd = torch.from_numpy(full.view(np.int16)).cuda()[:, :cols]
+    amax = dev_scalar(0.0)
+    lib.quantize_blockscale(xd, None, amax=amax)
+    assert host(amax)[0] == quantize.tensor_amax(bits)
+    big = dev_scalar(1e30)
+    lib.quantize_blockscale(xd, None, amax=big)
+    assert host(big)[0] == np.float32(1e30)
+    bits2 = bits.copy()
+    bits2[rows - 1, cols - 1] = 0x7FC0
+    full[:, :cols] = bits2
+    xd2 = torch.from_numpy(full.view(np.int16)).cuda()[:, :cols]
+    nan_amax = dev_scalar(0.0)
+    lib.quantize_blockscale(xd2, None, amax=nan_amax)
+    assert np.isnan(host(nan_amax)[0])
