@@ -22,6 +22,8 @@ over the 8192 x 4096 heavy-tailed activation workload with 8 rotating
 HBM-resident buffer sets (the quantizer's bandwidth roofline).
 `epilogue_fusion` times the largest fprop of the step with its output fused
 for the next layer (bf16 Y and its amax) against the fp32 output.
+`native_mxfp4` times the native MXFP4 comparison GEMM at the step's GEMM
+shape: its ratio to the UE5M3 GEMM is the cost of emulating UE5M3 scales.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 `--copy-calibration` instead runs a plain 256 MiB device copy, whose
@@ -248,6 +250,7 @@ def main():
     }
     step_elems = sum(t.elems for t in tensors)
     result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
+    result["native_mxfp4"] = native_mxfp4(lib, torch, gemm_tflops)
     del layers, tensors
     torch.cuda.empty_cache()
     if not args.no_quantize_only:
@@ -282,6 +285,50 @@ def epilogue_fusion(lib, torch, up):
         ms = e0.elapsed_time(e1) / 10
         res[name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
                      "output_bytes": tokens * out_f * (4 if name == "fp32_out" else 2)}
+    return res
+
+
+def native_mxfp4(lib, torch, ue5m3_tflops):
+    """The cost of emulating UE5M3: the native MXFP4 comparison GEMM (E2M1 +
+    E8M0 per 32 on the scaled FP4 MFMA, same tiling) at 8192 x 4096 x 16384
+    on random operands, against the UE5M3 GEMM's average in the step; and,
+    when this torch build provides it, the vendor library's MXFP4 GEMM."""
+    M, N, K = TOKENS, HIDDEN, FFN
+    g = torch.Generator(device="cuda").manual_seed(17)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    bc = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    asc = torch.randint(110, 140, (M, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    bsc = torch.randint(110, 140, (N, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    one = torch.ones(1, device="cuda")
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    flop = 2.0 * M * N * K
+
+    def timed(fn, iters=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms = timed(lambda: lib.gemm_nt_mxfp4(ac, asc, one, bc, bsc, one, c))
+    tf = flop / (ms * 1e-3) / 1e12
+    res = {"shape": f"{M}x{N}x{K}", "ms": round(ms, 4), "tflops": round(tf, 1),
+           "peak_fp4": 10100.0, "frac": round(tf / 10100.0, 4),
+           "emulation_tax": round(tf / ue5m3_tflops, 3)}
+    try:  # vendor comparison point, if supported by this torch build
+        a4 = ac.view(torch.float4_e2m1fn_x2)
+        b4 = bc.view(torch.float4_e2m1fn_x2)
+        ms_v = timed(lambda: torch._scaled_mm(a4, b4.t(), scale_a=asc.view(torch.float8_e8m0fnu),
+                                              scale_b=bsc.view(torch.float8_e8m0fnu),
+                                              out_dtype=torch.bfloat16))
+        res["vendor_mxfp4_bf16_out"] = {"ms": round(ms_v, 4), "tflops": round(flop / (ms_v * 1e-3) / 1e12, 1)}
+    except Exception as ex:  # pragma: no cover
+        res["vendor_mxfp4_bf16_out"] = f"unavailable: {type(ex).__name__}"
     return res
 
 

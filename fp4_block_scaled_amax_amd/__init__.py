@@ -33,6 +33,7 @@ _SIGNATURES = {
     "ue5m3fp4_dequantize": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt_bf16": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_nt_mxfp4": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_fprop": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_dgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_wgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
@@ -212,6 +213,25 @@ def gemm_nt_bf16(a, b, out, amax=None, stream=None):
                                               _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
                                               b.rows, a.cols, _ptr(out), _ptr(amax), _stream(stream))
     _check(st, "ue5m3fp4_gemm_nt_bf16")
+    return out
+
+
+def gemm_nt_mxfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out, stream=None):
+    """Native MXFP4 comparison GEMM: out[M][N] = tsA * tsB * A B^T with E2M1
+    codes ([rows][K/2]) and E8M0 scales per 32 elements ([rows][K/32])."""
+    import torch
+
+    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _require(t, (torch.uint8,), n, 2)
+    m, k = a_codes.shape[0], a_codes.shape[1] * 2
+    n = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != k or tuple(a_scales.shape) != (m, k // 32) or tuple(b_scales.shape) != (n, k // 32):
+        raise ValueError("MXFP4 operand shapes disagree")
+    _gemm_out(out, m, n)
+    st = load_library().ue5m3fp4_gemm_nt_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(a_ts), _ptr(b_codes),
+                                               _ptr(b_scales), _ptr(b_ts), m, n, k, _ptr(out),
+                                               _stream(stream))
+    _check(st, "ue5m3fp4_gemm_nt_mxfp4")
     return out
 
 

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libue5m3fp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_mx.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -158,6 +158,21 @@ int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_scales, const
                          stream);
 }
 
+int ue5m3fp4_gemm_nt_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                           int64_t M, int64_t N, int64_t K, float* c, void* stream) {
+    if (K >= 0 && K % 32 != 0) return UE5M3FP4_ESHAPE;
+    const int st = check_gemm(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c);
+    if (st != UE5M3FP4_OK || M == 0 || N == 0) return st;
+    GemmArgs g{a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, nullptr, nullptr};
+    if (K == 0) {  // an empty sum: the UE5M3 kernel writes the zeros
+        launch_gemm_nt(g, (hipStream_t)stream);
+        return launch_status();
+    }
+    launch_gemm_nt_mx(g, (hipStream_t)stream);
+    return launch_status();
+}
+
 int ue5m3fp4_gemm_fprop(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_ts,
                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
                         int64_t tokens, int64_t in_features, int64_t out_features, float* y,

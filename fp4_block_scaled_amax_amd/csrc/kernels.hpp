@@ -50,4 +50,8 @@ struct GemmArgs {
 
 void launch_gemm_nt(const GemmArgs& g, hipStream_t stream);
 
+// Native MXFP4 comparison GEMM: a_scales / b_scales are E8M0 bytes, one per
+// 32 elements along K ([rows][K/32]); fp32 output.
+void launch_gemm_nt_mx(const GemmArgs& g, hipStream_t stream);
+
 }  // namespace ue5m3fp4

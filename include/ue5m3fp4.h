@@ -158,6 +158,19 @@ UE5M3FP4_API int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_
                           int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
                           void* stream);
 
+/* Native MXFP4 comparison GEMM: the block format gfx950's scaled FP4 MFMA
+ * takes natively (OCP Microscaling: E2M1 elements, one E8M0 scale 2^(c-127)
+ * per 32 elements, 0xFF = NaN), with the same tensor-scale epilogue as
+ * ue5m3fp4_gemm_nt:  C = (tsA * tsB) * sum_k A(i,k) B(j,k), fp32 [M][N].
+ * It measures what emulating UE5M3 block-16 costs (UE5M3 paper, abstract:
+ * UE5M3 is software-emulated; format-aware fusion article: the MXFP4
+ * route).  a_codes [M][K/2], b_codes [N][K/2] (element 2j in the low nibble);
+ * a_scales [M][K/32], b_scales [N][K/32] E8M0 bytes.  K % 32 == 0
+ * (UE5M3FP4_ESHAPE otherwise); alignment and sizes as ue5m3fp4_gemm_nt. */
+UE5M3FP4_API int ue5m3fp4_gemm_nt_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                           int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
 /* fprop: Y = X W^T.  UFP4 paper, abstract (three training GEMMs).
  *   x: X [tokens][in] quantized row-wise (codes [tokens][in/2]);
  *   w: W [out][in] quantized row-wise (codes [out][in/2]);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -123,6 +123,16 @@ def test_gemm_bf16_argument_checks(L):
     assert g(P, P, P, P, P, P, 4, 4, 16, P, P + 2, None) == EALIGN       # amax alignment
     assert g(P, P, P, P, P, P, 1 << 31, 4, 16, P, None, None) == ERANGE
     assert g(None, None, None, None, None, None, 4, 0, 16, None, None, None) == OK  # empty
+
+
+def test_gemm_mxfp4_argument_checks(L):
+    g = L.ue5m3fp4_gemm_nt_mxfp4
+    assert g(P, P, P, P, P, P, 4, 4, 48, P, None) == ESHAPE       # K % 32
+    assert g(P, P, P, P, P, P, -1, 4, 32, P, None) == EINVAL
+    assert g(None, P, P, P, P, P, 4, 4, 32, P, None) == EINVAL
+    assert g(P, P, P, P, P, P, 4, 4, 32, P + 4, None) == EALIGN
+    assert g(P, P, P, P, P, P, 1 << 31, 4, 32, P, None) == ERANGE
+    assert g(None, None, None, None, None, None, 0, 4, 32, None, None) == OK
 
 
 def test_fprop_dgrad_wgrad_contract_the_right_axis(L):
