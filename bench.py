@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantize-only", action="store_true",
                    help="skip the stand-alone quantizer measurement")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the epilogue-fusion and native-MXFP4 comparisons")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -249,8 +251,9 @@ def main():
                      "rne": q_stats(lib.RNE), "sr": q_stats(lib.SR)},
     }
     step_elems = sum(t.elems for t in tensors)
-    result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
-    result["native_mxfp4"] = native_mxfp4(lib, torch, gemm_tflops)
+    if not args.no_extras:
+        result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
+        result["native_mxfp4"] = native_mxfp4(lib, torch, gemm_tflops)
     del layers, tensors
     torch.cuda.empty_cache()
     if not args.no_quantize_only:
