@@ -30,6 +30,9 @@ _SIGNATURES = {
     "ue5m3fp4_quantize_blockscale": [_c_void_p, _i64, _i64, _i64, _c_void_p, ctypes.c_int,
                                      ctypes.c_uint64, ctypes.c_uint32, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "ue5m3fp4_quantize_blockscale_2d": [_c_void_p, _i64, _i64, _i64, _c_void_p, ctypes.c_int,
+                                        ctypes.c_uint64, ctypes.c_uint32, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "ue5m3fp4_dequantize": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt_bf16": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p],
@@ -131,11 +134,8 @@ def empty_quantized(rows, cols, ts, device=None):
                      torch.empty((rows, cols // 16), dtype=torch.uint8, device=device), ts)
 
 
-def quantize_blockscale(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=None, col=None,
-                        amax=None, stream=None):
-    """Quantize a bf16 (rows x cols) tensor.  row / col: Quantized outputs (or
-    (codes, scales) pairs) for the row-wise and the transposed orientation, or
-    None.  amax: device fp32 scalar that receives max(amax, max|x|)."""
+def _quantize_operands(x, tensor_scale, row, col, amax):
+    """Check and unpack the arguments shared by the quantizer entry points."""
     import torch
 
     _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2)
@@ -158,10 +158,32 @@ def quantize_blockscale(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=Non
         raise ValueError("row output buffers have the wrong shape")
     if cc is not None and (tuple(cc.shape) != (cols, rows // 2) or tuple(cs.shape) != (cols, rows // 16)):
         raise ValueError("col output buffers have the wrong shape")
+    return rows, cols, rc, rs, cc, cs
+
+
+def quantize_blockscale(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=None, col=None,
+                        amax=None, stream=None):
+    """Quantize a bf16 (rows x cols) tensor.  row / col: Quantized outputs (or
+    (codes, scales) pairs) for the row-wise and the transposed orientation, or
+    None.  amax: device fp32 scalar that receives max(amax, max|x|)."""
+    rows, cols, rc, rs, cc, cs = _quantize_operands(x, tensor_scale, row, col, amax)
     st = load_library().ue5m3fp4_quantize_blockscale(
         _ptr(x), rows, cols, x.stride(0), _ptr(tensor_scale), int(rounding), int(seed),
         int(offset), _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs), _ptr(amax), _stream(stream))
     _check(st, "ue5m3fp4_quantize_blockscale")
+
+
+def quantize_blockscale_2d(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=None, col=None,
+                           amax=None, stream=None):
+    """Quantize with one scale per 16 x 16 tile (transposition-invariant):
+    the same arguments and output layouts as quantize_blockscale, the tile
+    scale repeated over its rows / columns; col codes are the transpose of
+    the row codes.  rows and cols must be multiples of 16."""
+    rows, cols, rc, rs, cc, cs = _quantize_operands(x, tensor_scale, row, col, amax)
+    st = load_library().ue5m3fp4_quantize_blockscale_2d(
+        _ptr(x), rows, cols, x.stride(0), _ptr(tensor_scale), int(rounding), int(seed),
+        int(offset), _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs), _ptr(amax), _stream(stream))
+    _check(st, "ue5m3fp4_quantize_blockscale_2d")
 
 
 def dequantize(q, out, stream=None):

@@ -105,6 +105,24 @@ int ue5m3fp4_quantize_blockscale(const uint16_t* x, int64_t rows, int64_t cols, 
     return launch_status();
 }
 
+int ue5m3fp4_quantize_blockscale_2d(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                    const float* tensor_scale, int rounding, uint64_t seed,
+                                    uint32_t offset, uint8_t* row_codes, uint8_t* row_scales,
+                                    uint8_t* col_codes, uint8_t* col_scales, float* amax_inout,
+                                    void* stream) {
+    if (!row_codes && !row_scales && !col_codes && !col_scales) return UE5M3FP4_EINVAL;
+    const int st = check_quantize(x, rows, cols, ld, tensor_scale, rounding, row_codes, row_scales,
+                                  col_codes, col_scales, amax_inout);
+    if (st != UE5M3FP4_OK) return st;
+    if (rows % 16 != 0) return UE5M3FP4_ESHAPE;
+    if (rows == 0 || cols == 0) return UE5M3FP4_OK;
+    QuantizeArgs a{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
+                   seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
+                   amax_inout};
+    launch_quantize_2d(a, (hipStream_t)stream);
+    return launch_status();
+}
+
 int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                       float max_safe, int rounding, uint64_t seed, uint32_t offset,
                                       uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,

@@ -23,6 +23,9 @@ struct QuantizeArgs {
 
 void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t stream);
 
+// 16 x 16 tile scales (rows and cols multiples of 16, at least one output).
+void launch_quantize_2d(const QuantizeArgs& a, hipStream_t stream);
+
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                        int64_t rows, int64_t cols, float* out, hipStream_t stream);
 

@@ -535,6 +535,203 @@ void dispatch_sr(const QuantizeArgs& a, hipStream_t s) {
     else dispatch_amax<ROW, COL, false>(a, s);
 }
 
+// ------------------------------------------------- 2-D (16 x 16) blocks --
+//
+// Transposition-invariant scaling ("Stable FP4 Training via Transposition-
+// Invariant Block Quantization", related-papers summary): one UE5M3 scale per
+// aligned 16 x 16 tile, each element rounded once, and the transposed operand
+// made of the same codes.  A 256-thread workgroup owns a 64 x 256 tile; wave
+// w holds tile rows 16w .. 16w + 15, lane (h, u) = (lane / 32, lane % 32)
+// loading 16-byte unit u (8 columns) of rows 16w + h + 2k, k < 8 (a wave
+// reads 2 rows x 512 bytes per load).  The 16 x 16 block b lives in lanes
+// (h, 2b) and (h, 2b + 1): one DPP swap and one exchange across the wave
+// halves give every one of its four lanes the tile amax.  Codes are computed
+// row-wise only (stochastic rounding draws the row-wise counter stream); the
+// transposed output is an 8 x 8 nibble transpose of the packed row codes
+// through LDS, with no second rounding.
+
+__device__ __forceinline__ void swap_bits(uint32_t& x, uint32_t& y, int s, uint32_t m) {
+    const uint32_t d = ((x >> s) ^ y) & m;
+    y ^= d;
+    x ^= d << s;
+}
+
+// w[i] holds 8 codes of row i (column j in nibble j); afterwards w[j] holds
+// the 8 codes of column j (row i in nibble i).  Three rounds of masked swaps:
+// nibbles within bytes, bytes within halfwords, halfwords within words.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t (&w)[8]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) swap_bits(w[2 * a], w[2 * a + 1], 4, 0x0F0F0F0Fu);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        swap_bits(w[4 * c], w[4 * c + 2], 8, 0x00FF00FFu);
+        swap_bits(w[4 * c + 1], w[4 * c + 3], 8, 0x00FF00FFu);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) swap_bits(w[m], w[4 + m], 16, 0x0000FFFFu);
+}
+
+constexpr int k2dRows = 64;   // tile rows: 4 waves x 16
+constexpr int k2dWords = 33;  // LDS words per tile row of packed codes (32 + 1: conflict-free columns)
+
+template <bool ROW, bool COL, bool SR, bool AMAX>
+__global__ __launch_bounds__(kThreads) void quantize2d_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ tensor_scale, uint64_t seed, uint32_t offset,
+    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
+    float* __restrict__ amax_inout) {
+    __shared__ uint32_t packed_lds[COL ? k2dRows * k2dWords : 1];
+    __shared__ uint8_t tcode[COL ? 4 * 16 : 1];
+    __shared__ float rlut[256];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int u = lane & 31, h = lane >> 5;
+    int64_t R0, C0;
+    tile_of<k2dRows>((uint32_t)((rows + k2dRows - 1) / k2dRows), (uint32_t)((cols + kTileCols - 1) / kTileCols),
+                     R0, C0);
+    const bool interior = R0 + k2dRows <= rows && C0 + kTileCols <= cols;
+
+    // ---- loads (edge addresses clamped into the tensor: rows and cols are
+    // multiples of 16, so a clamped value only ever shares a 16 x 16 block
+    // with other clamped values, and never reaches an output)
+    const int64_t c0 = C0 + 8 * u;
+    const bool col_ok = c0 < cols;
+    const int64_t rb = R0 + 16 * wv + h;  // row of k = 0; row k is rb + 2k
+    u32x4 w[8];
+    {
+        const uint16_t* src = x + (col_ok ? c0 : cols - 8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t r = min(rb + 2 * k, rows - 1);
+            w[k] = *reinterpret_cast<const u32x4*>(src + r * ld);
+        }
+    }
+
+    Ctx ctx;
+    ctx.ts = *tensor_scale;
+    ctx.K = 6.0f * ctx.ts;
+    ctx.yK = 1.0f / ctx.K;
+    ctx.fastK = ctx.K >= 0x1p-100f && ctx.K <= 0x1p100f;
+    ctx.tinyOK = ctx.K >= 1.0f;
+    rlut[t] = rcp_entry((uint32_t)t, ctx.ts);
+
+    // ---- tile amax (bf16 magnitude bits; NaN sorts above Inf)
+    uint32_t m2 = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        m2 = pk_max_u16(m2, pk_max_u16(pk_max_u16(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu),
+                                       pk_max_u16(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu)));
+    const uint32_t tmax = max(m2 & 0xFFFFu, m2 >> 16);
+    uint32_t amax16 = max(tmax, swap_pair(tmax));
+    amax16 = max(amax16, (uint32_t)__shfl_xor((int)amax16, 32));
+    __syncthreads();  // reciprocal table visible
+
+    // ---- codes, once.  The four lanes of a block hold the same amax, so
+    // they take the same path.
+    bool ok = ctx.fastK;
+    BlockScale b = block_scale(amax16, ctx, rlut, ok);
+    uint32_t packed[8];
+    if (__builtin_expect(ok, 1)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float v[8];
+            unpack8(w[k], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * b.r;
+            U32x4 rnd;
+            if (SR) rnd = sr_words(((uint64_t)(rb + 2 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+            packed[k] = encode8<SR>(v, rnd);
+        }
+    } else {
+        b = block_scale_general(amax16, ctx.ts, ctx.K);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            U32x4 rnd;
+            if (SR) rnd = sr_words(((uint64_t)(rb + 2 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+            packed[k] = encode8_general<SR>(w[k], b.code, b.r, rnd);
+        }
+    }
+
+    // ---- row-wise output: codes of rows rb + 2k; the block's scale byte is
+    // repeated on its 16 rows (the even lane of the pair writes rows k < 4,
+    // the odd lane rows k >= 4)
+    if (ROW) {
+        uint8_t* pc = row_codes + rb * (cols / 2) + c0 / 2;
+        uint8_t* ps = row_scales + rb * (cols / 16) + c0 / 16;
+        const int64_t cstep = 2 * (cols / 2), sstep = 2 * (cols / 16);
+        const int k0 = 4 * (u & 1);
+        if (interior) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ps[(k0 + k) * sstep] = (uint8_t)b.code;
+        } else if (col_ok) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (rb + 2 * k < rows) {
+                    *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+                    if ((k >> 2) == (u & 1)) ps[k * sstep] = (uint8_t)b.code;
+                }
+            }
+        }
+    }
+
+    // ---- transposed output: thread (q, v) = (t % 8, t / 8) transposes the
+    // 8 x 8 code block of tile rows 8q .. 8q + 7 and columns 8v .. 8v + 7; the
+    // 8 threads of a column group write its 64 tile rows as 32 contiguous
+    // bytes.  Thread t writes the scale bytes of tile column t.
+    if (COL) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) packed_lds[(16 * wv + h + 2 * k) * k2dWords + u] = packed[k];
+        if (h == 0 && (u & 1) == 0) tcode[16 * wv + (u >> 1)] = (uint8_t)b.code;
+        __syncthreads();
+        const int q = t & 7, vcol = t >> 3;
+        uint32_t cw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cw[i] = packed_lds[(8 * q + i) * k2dWords + vcol];
+        transpose_nibbles8(cw);
+        const int64_t r8 = R0 + 8 * q, cb = C0 + 8 * vcol;
+        uint8_t* dst = col_codes + cb * (rows / 2) + r8 / 2;
+        if (interior || (r8 < rows && cb < cols)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(dst + j * (rows / 2)) = cw[j];
+        }
+        const int64_t c = C0 + t;
+        if (c < cols) {
+            const int blk = t >> 4;
+            uint8_t* sd = col_scales + c * (rows / 16) + R0 / 16;
+            if (R0 + k2dRows <= rows && (rows / 16) % 4 == 0) {
+                *reinterpret_cast<uint32_t*>(sd) = (uint32_t)tcode[blk] | ((uint32_t)tcode[16 + blk] << 8) |
+                                                   ((uint32_t)tcode[32 + blk] << 16) |
+                                                   ((uint32_t)tcode[48 + blk] << 24);
+            } else {
+                for (int g = 0; g < 4 && R0 + 16 * g < rows; ++g) sd[g] = tcode[16 * g + blk];
+            }
+        }
+    }
+
+    if (AMAX) amax_commit(tmax, amax_inout);
+}
+
+template <bool ROW, bool COL, bool SR, bool AMAX>
+void launch_quantize2d_t(const QuantizeArgs& a, hipStream_t stream) {
+    const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + k2dRows - 1) / k2dRows);
+    hipLaunchKernelGGL((quantize2d_kernel<ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, a.x, a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
+                       a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
+}
+
+template <bool ROW, bool COL>
+void dispatch_2d(const QuantizeArgs& a, hipStream_t s) {
+    if (a.stochastic) {
+        if (a.amax_inout) launch_quantize2d_t<ROW, COL, true, true>(a, s);
+        else launch_quantize2d_t<ROW, COL, true, false>(a, s);
+    } else {
+        if (a.amax_inout) launch_quantize2d_t<ROW, COL, false, true>(a, s);
+        else launch_quantize2d_t<ROW, COL, false, false>(a, s);
+    }
+}
+
 // ----------------------------------------------------------- dequantize --
 
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ codes,
@@ -616,6 +813,14 @@ void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t s) {
     else if (row) dispatch_sr<true, false>(a, s);
     else if (col) dispatch_sr<false, true>(a, s);
     else launch_amax(a, s);  // amax-only pass
+}
+
+void launch_quantize_2d(const QuantizeArgs& a, hipStream_t s) {
+    const bool row = a.row_codes != nullptr;
+    const bool col = a.col_codes != nullptr;
+    if (row && col) dispatch_2d<true, true>(a, s);
+    else if (row) dispatch_2d<true, false>(a, s);
+    else dispatch_2d<false, true>(a, s);
 }
 
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,

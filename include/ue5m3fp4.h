@@ -110,6 +110,30 @@ UE5M3FP4_API int ue5m3fp4_quantize_blockscale(const uint16_t* x, int64_t rows, i
                                  uint8_t* col_codes, uint8_t* col_scales, float* amax_inout,
                                  void* stream);
 
+/* Quantize x with one UE5M3 scale per aligned 16 x 16 tile instead of per
+ * 16-element row block ("Stable FP4 Training via Transposition-Invariant
+ * Block Quantization", summary in the UE5M3 paper's related-papers list:
+ * 2-D blocks give a value the same scale in the forward operand and in the
+ * transposed operand of the backward GEMMs).  Per tile: amax over its 256
+ * elements, the block-scale and element steps of ue5m3fp4_quantize_blockscale
+ * with that amax; each element is rounded once (SR bits: the row-wise stream
+ * of ue5m3fp4_quantize_blockscale with the same seed/offset), so col_codes is
+ * exactly the transpose of row_codes.
+ *   row_codes/row_scales, col_codes/col_scales: the layouts of
+ *       ue5m3fp4_quantize_blockscale, the tile's scale byte repeated on each
+ *       of its 16 rows (row_scales[i][J] = tile (i/16, J)) and columns
+ *       (col_scales[j][I] = tile (I, j/16)), so the GEMM entry points take
+ *       either output unchanged.  At least one pair is required (EINVAL).
+ *   amax_inout, rounding, seed, offset, tensor_scale: as
+ *       ue5m3fp4_quantize_blockscale.
+ * Requirements: rows % 16 == 0 and cols % 16 == 0 (ESHAPE); other rules as
+ * ue5m3fp4_quantize_blockscale. */
+UE5M3FP4_API int ue5m3fp4_quantize_blockscale_2d(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                    const float* tensor_scale, int rounding, uint64_t seed,
+                                    uint32_t offset, uint8_t* row_codes, uint8_t* row_scales,
+                                    uint8_t* col_codes, uint8_t* col_scales, float* amax_inout,
+                                    void* stream);
+
 /* Current-tensor scaling, the alternative to the periodic refresh: the
  * tensor scale comes from this tensor's own amax, which costs one more read
  * of x (UE5M3 paper, abstract: the UE5M3 range is what lets the recipe use

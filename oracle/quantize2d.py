@@ -53,8 +53,10 @@ def tile_codes(x_bits, ts):
     return formats.ue5m3_encode(s_raw).astype(np.uint8)
 
 
-def element_codes(x_bits, ts, rounding=RNE, seed=0, offset=0):
-    """E2M1 code (0..15) of every element, shape (R, C), and the tile codes."""
+def element_codes(x_bits, ts, rounding=RNE, seed=0, offset=0, row0=0):
+    """E2M1 code (0..15) of every element, shape (R, C), and the tile codes.
+    row0: x holds rows row0 .. row0 + R - 1 of a larger tensor with the same
+    columns (a multiple of 16); the stochastic-rounding bits use the true row."""
     x = formats.bf16_to_f32(np.asarray(x_bits, dtype=np.uint16))
     R, C = x.shape
     ts = np.float32(ts)
@@ -71,7 +73,7 @@ def element_codes(x_bits, ts, rounding=RNE, seed=0, offset=0):
     if rounding == RNE:
         idx = formats.e2m1_round_nearest_even(a)
     else:
-        u16 = philox.sr_bits(seed, offset, 0, R, C)
+        u16 = philox.sr_bits(seed, offset, 0, None, C, rows=np.arange(row0, row0 + R))
         idx = formats.e2m1_round_stochastic(a, u16)
     idx = np.where(special, 0, idx).astype(np.uint8)
     sign = np.signbit(x).astype(np.uint8)
@@ -82,13 +84,14 @@ def _pack(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-def quantize_blockscale_2d(x_bits, ts, rounding=RNE, seed=0, offset=0):
+def quantize_blockscale_2d(x_bits, ts, rounding=RNE, seed=0, offset=0, row0=0):
     """Quantize a bf16 tensor (uint16 bits, (R, C)) with 16 x 16 tile scales.
 
     Returns (row_codes (R, C/2), row_scales (R, C/16), col_codes (C, R/2),
-    col_scales (C, R/16), tile_codes (R/16, C/16)), all uint8.
+    col_scales (C, R/16), tile_codes (R/16, C/16)), all uint8.  row0: as
+    element_codes (a 16-aligned slice of rows of a larger tensor).
     """
-    codes, code_t = element_codes(x_bits, ts, rounding, seed, offset)
+    codes, code_t = element_codes(x_bits, ts, rounding, seed, offset, row0)
     row_codes = _pack(codes)
     col_codes = _pack(np.ascontiguousarray(codes.T))
     row_scales = np.repeat(code_t, 16, axis=0)

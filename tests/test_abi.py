@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -72,6 +72,28 @@ def test_quantize_argument_checks(L):
     # empty tensors are valid no-ops and touch nothing (even NULL pointers)
     assert q(L, rows=0, x=None, rc=None, rs=None, cc=None, cs=None) == OK
     assert q(L, cols=0, ld=0, x=None) == OK
+
+
+def q2(L, x=P, rows=32, cols=32, ld=32, ts=P, rnd=0, rc=P, rs=P, cc=P, cs=P, amax=None):
+    return L.ue5m3fp4_quantize_blockscale_2d(x, rows, cols, ld, ts, rnd, 0, 0, rc, rs, cc, cs, amax,
+                                             None)
+
+
+def test_quantize_2d_argument_checks(L):
+    assert q2(L, rows=-1) == EINVAL
+    assert q2(L, rnd=2) == EINVAL
+    assert q2(L, x=None) == EINVAL
+    assert q2(L, rc=None) == EINVAL             # half of a pair
+    assert q2(L, rc=None, rs=None, cc=None, cs=None, amax=P) == EINVAL  # no output
+    assert q2(L, ts=None) == EINVAL
+    assert q2(L, cols=40, ld=40) == ESHAPE      # cols % 16
+    assert q2(L, rows=40, cc=None, cs=None) == ESHAPE  # rows % 16, even row-only
+    assert q2(L, ld=16) == ESHAPE
+    assert q2(L, ld=36) == EALIGN
+    assert q2(L, cc=P + 4) == EALIGN
+    assert q2(L, amax=P + 2) == EALIGN
+    assert q2(L, rows=1 << 31) == ERANGE
+    assert q2(L, rows=0, x=None) == OK          # empty tensor: nothing launched
 
 
 def qc(L, x=P, rows=32, cols=32, ld=32, ms=7168.0, rnd=0, rc=P, rs=P, cc=P, cs=P, ts=P, amax=P):

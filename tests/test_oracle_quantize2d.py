@@ -151,3 +151,15 @@ def test_shape_validation():
         quantize2d.tile_codes(np.zeros((16, 24), dtype=np.uint16), 1.0)
     with pytest.raises(ValueError):
         quantize2d.tile_codes(np.zeros((8, 16), dtype=np.uint16), 1.0)
+
+
+def test_row_slice_matches_full():
+    """A 16-aligned slice of rows (row0) reproduces those rows of the whole
+    tensor's result, stochastic bits included."""
+    xb = random_bf16((96, 48), 61, "gradient")
+    ts = np.float32(quantize.tensor_amax(xb) / np.float32(43008.0))
+    full = quantize2d.quantize_blockscale_2d(xb, ts, quantize.SR, seed=3, offset=4)
+    part = quantize2d.quantize_blockscale_2d(xb[32:64], ts, quantize.SR, seed=3, offset=4, row0=32)
+    np.testing.assert_array_equal(part[0], full[0][32:64])
+    np.testing.assert_array_equal(part[1], full[1][32:64])
+    np.testing.assert_array_equal(part[2], full[2][:, 16:32])
