@@ -339,7 +339,8 @@ def quantize_only(lib, torch):
     """The quantizer alone on the 8192 x 4096 heavy-tailed activation workload
     (Student-t x normal body, 16 outlier columns x100): row-wise only and
     row-wise + transposed, round-to-nearest and stochastic, tensor amax on;
-    and the current-tensor-scaling variant (amax pass + scale + quantize).
+    the current-tensor-scaling variant (amax pass + scale + quantize); and
+    the 2-D (16 x 16 tile) variant, both outputs from one rounding.
     8 device copies of the input and 8 output sets rotate (about 840 MB) so
     every launch reads and writes HBM, not the 256 MB cache.  GB/s counts the
     algorithmic bytes: 2 per element read, 0.5625 per element per output."""
@@ -364,10 +365,15 @@ def quantize_only(lib, torch):
                                      ("rne_row_col", lib.RNE, True, False),
                                      ("sr_row", lib.SR, False, False),
                                      ("sr_row_col", lib.SR, True, False),
-                                     ("current_scaling_rne_row_col", lib.RNE, True, True)):
+                                     ("current_scaling_rne_row_col", lib.RNE, True, True),
+                                     ("tile2d_rne_row_col", lib.RNE, True, False),
+                                     ("tile2d_sr_row_col", lib.SR, True, False)):
         def run(i):
             k = i % sets
-            if current:
+            if name.startswith("tile2d"):
+                lib.quantize_blockscale_2d(xs[k], ts, rnd, sr_seed(2), i, row=outs[k][0], col=outs[k][1],
+                                           amax=amax)
+            elif current:
                 lib.quantize_current_scaling(xs[k], ts_cur, amax, rnd, sr_seed(2), i, row=outs[k][0],
                                              col=outs[k][1] if both else None)
             else:
