@@ -266,7 +266,10 @@ def main():
 def epilogue_fusion(lib, torch, up):
     """The up projection's fprop (8192 x 16384 x 4096, the largest output of
     the step) with its output fused for the next layer -- bf16 Y plus its
-    tensor amax -- against the fp32 output, on the same quantized operands."""
+    tensor amax, and optionally Y's block-16 quantization (row-wise and
+    transposed, round to nearest) in the epilogue -- against the fp32 output
+    and against the bf16 output followed by the stand-alone quantizer, on the
+    same quantized operands."""
     X, W = up[0], up[1]
     tokens, out_f = X.row.rows, W.row.rows
     y32 = torch.empty((tokens, out_f), dtype=torch.float32, device="cuda")
@@ -274,8 +277,19 @@ def epilogue_fusion(lib, torch, up):
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     flop = 2.0 * tokens * out_f * X.row.cols
     res = {"shape": f"{tokens}x{out_f}x{X.row.cols}"}
+    # the next linear's input quantization (block-16, both orientations,
+    # round to nearest) fused into the epilogue, and done after it
+    ts_y = torch.full((1,), 1.0 / 43008.0, dtype=torch.float32, device="cuda")
+    qr = lib.empty_quantized(tokens, out_f, ts_y)
+    qc = lib.empty_quantized(out_f, tokens, ts_y)
     for name, fn in (("fp32_out", lambda: lib.gemm_fprop(X.row, W.row, y32)),
-                     ("bf16_out_amax", lambda: lib.gemm_nt_bf16(X.row, W.row, y16, amax=amax))):
+                     ("bf16_out_amax", lambda: lib.gemm_nt_bf16(X.row, W.row, y16, amax=amax)),
+                     ("bf16_out_amax_quantized_in_epilogue",
+                      lambda: lib.gemm_nt_bf16_quantized(X.row, W.row, y16, ts_y, lib.RNE, row=qr, col=qc,
+                                                         amax=amax)),
+                     ("bf16_out_amax_then_quantize",
+                      lambda: (lib.gemm_nt_bf16(X.row, W.row, y16, amax=amax),
+                               lib.quantize_blockscale(y16, ts_y, lib.RNE, row=qr, col=qc)))):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -288,6 +302,7 @@ def epilogue_fusion(lib, torch, up):
         ms = e0.elapsed_time(e1) / 10
         res[name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
                      "output_bytes": tokens * out_f * (4 if name == "fp32_out" else 2)}
+    del qr, qc
     return res
 
 

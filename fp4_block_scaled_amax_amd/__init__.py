@@ -36,6 +36,9 @@ _SIGNATURES = {
     "ue5m3fp4_dequantize": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_nt_bf16": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p],
+    "ue5m3fp4_gemm_nt_bf16_quantized": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p,
+                                                          _c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                                          ctypes.c_uint32] + [_c_void_p] * 5,
     "ue5m3fp4_gemm_nt_mxfp4": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_fprop": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
     "ue5m3fp4_gemm_dgrad": [_c_void_p] * 6 + [_i64, _i64, _i64, _c_void_p, _c_void_p],
@@ -235,6 +238,43 @@ def gemm_nt_bf16(a, b, out, amax=None, stream=None):
                                               _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
                                               b.rows, a.cols, _ptr(out), _ptr(amax), _stream(stream))
     _check(st, "ue5m3fp4_gemm_nt_bf16")
+    return out
+
+
+def gemm_nt_bf16_quantized(a, b, out, out_ts, rounding=RNE, seed=0, offset=0, row=None, col=None,
+                           amax=None, stream=None):
+    """gemm_nt_bf16 whose epilogue also quantizes the bf16 output for the next
+    linear: row / col (Quantized or (codes, scales), or None) receive exactly
+    what quantize_blockscale(out, out_ts, rounding, seed, offset, ...) would
+    write.  out_ts: the output's device fp32 tensor scale."""
+    import torch
+
+    if a.cols != b.cols:
+        raise ValueError("A and B disagree on K")
+    M, N = a.rows, b.rows
+    _require(out, (torch.bfloat16, torch.int16, torch.uint16), "out", 2)
+    if tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous ({M}, {N}) tensor")
+    _require(out_ts, (torch.float32,), "out_ts")
+    if amax is not None:
+        _require(amax, (torch.float32,), "amax")
+    rc = rs = cc = cs = None
+    if row is not None:
+        rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
+        if tuple(rc.shape) != (M, N // 2) or tuple(rs.shape) != (M, N // 16):
+            raise ValueError("row output buffers have the wrong shape")
+    if col is not None:
+        cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
+        if tuple(cc.shape) != (N, M // 2) or tuple(cs.shape) != (N, M // 16):
+            raise ValueError("col output buffers have the wrong shape")
+    for t, n in ((rc, "row codes"), (rs, "row scales"), (cc, "col codes"), (cs, "col scales")):
+        if t is not None:
+            _require(t, (torch.uint8,), n)
+    st = load_library().ue5m3fp4_gemm_nt_bf16_quantized(
+        _ptr(a.codes), _ptr(a.scales), _ptr(a.ts), _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), M, N,
+        a.cols, _ptr(out), _ptr(amax), _ptr(out_ts), int(rounding), int(seed), int(offset), _ptr(rc),
+        _ptr(rs), _ptr(cc), _ptr(cs), _stream(stream))
+    _check(st, "ue5m3fp4_gemm_nt_bf16_quantized")
     return out
 
 

@@ -76,14 +76,28 @@ int run_gemm(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_
 
 int run_gemm_bf16(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_t* bc,
                   const uint8_t* bs, const float* bt, int64_t M, int64_t N, int64_t K, uint16_t* c,
-                  float* amax, void* stream) {
+                  float* amax, const OutputQuant& q, void* stream) {
     const int st = check_gemm(ac, as, at, bc, bs, bt, M, N, K, c);
     if (st != UE5M3FP4_OK) return st;
     if (amax && !aligned4(amax)) return UE5M3FP4_EALIGN;
     if (M == 0 || N == 0) return UE5M3FP4_OK;
-    GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, nullptr, c, amax};
+    GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, nullptr, c, amax, q};
     launch_gemm_nt(g, (hipStream_t)stream);
     return launch_status();
+}
+
+// Arguments of the quantizing epilogue, checked before the GEMM's own.
+int check_output_quant(int64_t M, int64_t N, const float* ts, int rounding, const uint8_t* rc,
+                       const uint8_t* rs, const uint8_t* cc, const uint8_t* cs) {
+    if (!ts) return UE5M3FP4_EINVAL;
+    if (rounding != UE5M3FP4_RNE && rounding != UE5M3FP4_SR) return UE5M3FP4_EINVAL;
+    if ((rc == nullptr) != (rs == nullptr) || (cc == nullptr) != (cs == nullptr)) return UE5M3FP4_EINVAL;
+    if (!rc && !cc) return UE5M3FP4_EINVAL;  // no quantized output requested
+    if ((rc && N % 16 != 0) || (cc && M % 16 != 0)) return UE5M3FP4_ESHAPE;
+    if (!aligned4(ts) || (rc && (!aligned16(rc) || !aligned16(rs))) ||
+        (cc && (!aligned16(cc) || !aligned16(cs))))
+        return UE5M3FP4_EALIGN;
+    return UE5M3FP4_OK;
 }
 
 }  // namespace
@@ -173,6 +187,22 @@ int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
                           void* stream) {
     return run_gemm_bf16(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, amax_inout,
+                         OutputQuant{}, stream);
+}
+
+int ue5m3fp4_gemm_nt_bf16_quantized(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                                    int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
+                                    const float* c_tensor_scale, int rounding, uint64_t seed,
+                                    uint32_t offset, uint8_t* c_row_codes, uint8_t* c_row_scales,
+                                    uint8_t* c_col_codes, uint8_t* c_col_scales, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return UE5M3FP4_EINVAL;
+    const int st = check_output_quant(M, N, c_tensor_scale, rounding, c_row_codes, c_row_scales,
+                                      c_col_codes, c_col_scales);
+    if (st != UE5M3FP4_OK) return st;
+    const OutputQuant q{c_tensor_scale, c_row_codes, c_row_scales, c_col_codes, c_col_scales,
+                        seed, offset, rounding == UE5M3FP4_SR};
+    return run_gemm_bf16(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, amax_inout, q,
                          stream);
 }
 

@@ -53,6 +53,7 @@
 // 32 workgroups in flight on one XCD share 4 A panels and 8 B panels in L2.
 #include "formats.hpp"
 #include "kernels.hpp"
+#include "quant_block.hpp"
 
 namespace ue5m3fp4 {
 
@@ -74,6 +75,11 @@ constexpr int kStage = kScalesB + 8 * kScaleBlockStride;  // 53760 bytes
 constexpr int kLut = 2 * kStage;
 constexpr int kSmem = kLut + 256 * 4;
 constexpr int kGroupM = 4;  // tile rows per group in the tile order
+// quantizing epilogue: the 256 x 256 bf16 output tile (512 bytes per row,
+// 16-byte units XOR-swizzled by the row's 16-row block) and a reciprocal
+// table, reusing the staging buffers
+constexpr int kQTile = kBM * kBN * 2;
+constexpr int kSmemQ = kQTile + 256 * 4;
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100,
@@ -198,13 +204,135 @@ __device__ __forceinline__ void amax_commit(uint32_t m, float* amax) {
     }
 }
 
-template <bool ALIGNED, bool BF16>
+// Byte offset of element (row, col) of the bf16 output tile in LDS.
+__device__ __forceinline__ int qtile_offset(int row, int col) {
+    return row * (kBN * 2) + ((((col >> 3) ^ (row >> 4)) & 31) << 4) + ((col & 7) << 1);
+}
+
+// Row-wise block-16 quantization of the bf16 output tile held in LDS
+// (blocks along N): thread t takes 16-byte unit t % 32 of tile rows
+// t / 32 + 8k; the lane pair (t, t ^ 1) shares a block.  Output row m0 + row
+// of the M x N output, stochastic bits from orientation 0 of that shape.
+template <bool SR>
+__device__ __forceinline__ void quantize_tile_rows(const uint8_t* tile, const Ctx& ctx, const float* rlut,
+                                                   const OutputQuant& q, int64_t m0, int64_t n0,
+                                                   int64_t M, int64_t N) {
+    const int t = threadIdx.x, u = t & 31;
+    const int64_t gc = n0 + 8 * u;
+#pragma unroll 8
+    for (int k = 0; k < kBM / 8; ++k) {
+        const int row = (t >> 5) + 8 * k;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + qtile_offset(row, 8 * u));
+        const uint32_t m = max_abs8(w);
+        const uint32_t amax16 = max(m, swap_pair(m));  // both lanes of the block agree
+        bool ok = ctx.fastK;
+        BlockScale b = block_scale(amax16, ctx, rlut, ok);
+        const int64_t gr = m0 + row;
+        U32x4 rnd;
+        if (SR) rnd = sr_words(((uint64_t)gr * (uint64_t)N + (uint64_t)gc) >> 3, q.offset, 0u, q.seed);
+        uint32_t packed;
+        if (__builtin_expect(ok, 1)) {
+            float v[8];
+            unpack8(w, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * b.r;
+            packed = encode8<SR>(v, rnd);
+        } else {
+            b = block_scale_general(amax16, ctx.ts, ctx.K);
+            packed = encode8_general<SR>(w, b.code, b.r, rnd);
+        }
+        if (gr < M && gc < N) {
+            *reinterpret_cast<uint32_t*>(q.row_codes + gr * (N / 2) + gc / 2) = packed;
+            if ((u & 1) == 0) q.row_scales[gr * (N / 16) + gc / 16] = (uint8_t)b.code;
+        }
+    }
+}
+
+// Transposed block-16 quantization of the tile (blocks along M): in pass p
+// wave w takes 16-byte unit J = w + 4p (8 columns); lane (rb, cp) =
+// (lane % 16, lane / 16) reads the 4-byte column pair cp of J over tile rows
+// 16 rb .. 16 rb + 15 (64 distinct banks) and quantizes its two columns.
+template <bool SR>
+__device__ __forceinline__ void quantize_tile_cols(const uint8_t* tile, const Ctx& ctx, const float* rlut,
+                                                   const OutputQuant& q, int64_t m0, int64_t n0,
+                                                   int64_t M, int64_t N) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int rb = lane & 15, cp = lane >> 4;
+    const int64_t gr = m0 + 16 * rb;
+#pragma unroll 2
+    for (int p = 0; p < kBN / 32; ++p) {
+        const int J = wv + 4 * p;
+        const int c = 8 * J + 2 * cp;  // tile column of the pair's first column
+        uint32_t cw[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            cw[i] = *reinterpret_cast<const uint32_t*>(tile + qtile_offset(16 * rb + i, c));
+        uint32_t m2 = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m2 = pk_max_u16(m2, cw[i] & 0x7FFF7FFFu);
+        bool ok = ctx.fastK;
+        BlockScale ba = block_scale(m2 & 0xFFFFu, ctx, rlut, ok);
+        BlockScale bb = block_scale(m2 >> 16, ctx, rlut, ok);
+        const int64_t gca = n0 + c, gcb = gca + 1;
+        U32x4 rnd[4];
+        if (SR) {
+            const uint64_t na = ((uint64_t)gca * (uint64_t)M + (uint64_t)gr) >> 3;
+            const uint64_t nb = ((uint64_t)gcb * (uint64_t)M + (uint64_t)gr) >> 3;
+            rnd[0] = sr_words(na, q.offset, 1u, q.seed);
+            rnd[1] = sr_words(na + 1u, q.offset, 1u, q.seed);
+            rnd[2] = sr_words(nb, q.offset, 1u, q.seed);
+            rnd[3] = sr_words(nb + 1u, q.offset, 1u, q.seed);
+        }
+        uint32_t pa[2], pb[2];
+        if (__builtin_expect(ok, 1)) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                float va[8], vb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    va[i] = bf16_lo(cw[8 * hh + i]) * ba.r;
+                    vb[i] = bf16_hi(cw[8 * hh + i]) * bb.r;
+                }
+                pa[hh] = encode8<SR>(va, rnd[hh]);
+                pb[hh] = encode8<SR>(vb, rnd[2 + hh]);
+            }
+        } else {
+            ba = block_scale_general(m2 & 0xFFFFu, ctx.ts, ctx.K);
+            bb = block_scale_general(m2 >> 16, ctx.ts, ctx.K);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                uint32_t la[4], lb[4];  // per-column words of 8 rows
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w0 = cw[8 * hh + 2 * i], w1 = cw[8 * hh + 2 * i + 1];
+                    la[i] = (w0 & 0xFFFFu) | (w1 << 16);
+                    lb[i] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+                }
+                pa[hh] = encode8_general<SR>(u32x4{la[0], la[1], la[2], la[3]}, ba.code, ba.r, rnd[hh]);
+                pb[hh] = encode8_general<SR>(u32x4{lb[0], lb[1], lb[2], lb[3]}, bb.code, bb.r, rnd[2 + hh]);
+            }
+        }
+        if (gr < M) {
+            if (gca < N) {
+                *reinterpret_cast<u32x2*>(q.col_codes + gca * (M / 2) + gr / 2) = u32x2{pa[0], pa[1]};
+                q.col_scales[gca * (M / 16) + gr / 16] = (uint8_t)ba.code;
+            }
+            if (gcb < N) {
+                *reinterpret_cast<u32x2*>(q.col_codes + gcb * (M / 2) + gr / 2) = u32x2{pb[0], pb[1]};
+                q.col_scales[gcb * (M / 16) + gr / 16] = (uint8_t)bb.code;
+            }
+        }
+    }
+}
+
+template <bool ALIGNED, bool BF16, bool QUANT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, const float* __restrict__ b_ts, int64_t M, int64_t N,
-    int64_t K, float* __restrict__ C, uint16_t* __restrict__ Cb, float* __restrict__ amax) {
-    __shared__ __align__(16) uint8_t smem[kSmem];
+    int64_t K, float* __restrict__ C, uint16_t* __restrict__ Cb, float* __restrict__ amax,
+    OutputQuant q) {
+    __shared__ __align__(16) uint8_t smem[QUANT ? kSmemQ : kSmem];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem + kLut);
 
     const int tid = threadIdx.x;
@@ -378,10 +506,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     // ---- epilogue: C = (acc * 256 tsA) * tsB, stored as fp32, or rounded to
     // bf16 with the tensor amax of the stored values folded into *amax.
     // Accumulator register e of lane (r, h) holds row 8 * (e / 4) + 4 * h +
-    // e % 4, column r of a 32 x 32 tile.
+    // e % 4, column r of a 32 x 32 tile.  With QUANT the bf16 values also go
+    // to an LDS copy of the output tile, which is then quantized block-16
+    // (row-wise and/or transposed) under the output's tensor scale.
     const float sa256 = *a_ts * 256.0f, tsb = *b_ts;
     const int64_t row0 = m0 + wm * 128 + 4 * h, col0 = n0 + wn * 128 + r;
+    const int trow0 = wm * 128 + 4 * h, tcol0 = wn * 128 + r;  // within the tile
     uint32_t tmax = 0u;  // max |bf16| bits stored by this lane
+    if (QUANT) __syncthreads();  // every wave is done with the staging buffers
     if (m0 + kBM <= M && n0 + kBN <= N) {
         // interior tile: one row pointer per accumulator row, the 4 column
         // tiles at immediate offsets
@@ -397,6 +529,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
                         const uint16_t b = to_bf16(v);
                         Cb[off + j * 32] = b;
                         tmax = max(tmax, (uint32_t)(b & 0x7FFFu));
+                        if (QUANT)
+                            *reinterpret_cast<uint16_t*>(
+                                smem + qtile_offset(trow0 + i * 32 + 8 * (e >> 2) + (e & 3), tcol0 + j * 32)) = b;
                     } else {
                         C[off + j * 32] = v;
                     }
@@ -411,8 +546,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int64_t row = row0 + i * 32 + 8 * (e >> 2) + (e & 3);
+                    const float v = (acc[i][j][e] * sa256) * tsb;
                     if (row < M && col < N) {
-                        const float v = (acc[i][j][e] * sa256) * tsb;
                         if (BF16) {
                             const uint16_t b = to_bf16(v);
                             Cb[row * N + col] = b;
@@ -421,30 +556,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
                             C[row * N + col] = v;
                         }
                     }
+                    // outside the output: a value that shares no 16-block
+                    // with a stored one (the quantized axes are multiples of 16)
+                    if (QUANT)
+                        *reinterpret_cast<uint16_t*>(
+                            smem + qtile_offset(trow0 + i * 32 + 8 * (e >> 2) + (e & 3), tcol0 + j * 32)) =
+                            to_bf16(v);
                 }
             }
+    }
+    if (QUANT) {
+        float* rlut = reinterpret_cast<float*>(smem + kQTile);
+        const Ctx ctx = make_ctx(*q.ts);
+        rlut[tid] = rcp_entry((uint32_t)tid, ctx.ts);
+        __syncthreads();  // tile and table visible
+        if (q.row_codes) {
+            if (q.stochastic) quantize_tile_rows<true>(smem, ctx, rlut, q, m0, n0, M, N);
+            else quantize_tile_rows<false>(smem, ctx, rlut, q, m0, n0, M, N);
+        }
+        if (q.col_codes) {
+            if (q.stochastic) quantize_tile_cols<true>(smem, ctx, rlut, q, m0, n0, M, N);
+            else quantize_tile_cols<false>(smem, ctx, rlut, q, m0, n0, M, N);
+        }
     }
     if (BF16 && amax != nullptr) amax_commit(tmax, amax);
 }
 
 }  // namespace
 
-template <bool ALIGNED, bool BF16>
+template <bool ALIGNED, bool BF16, bool QUANT>
 void launch_gemm(const GemmArgs& g, hipStream_t stream) {
     const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-    hipLaunchKernelGGL((gemm_nt_kernel<ALIGNED, BF16>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
-                       g.a_codes, g.a_scales, g.a_ts, g.b_codes, g.b_scales, g.b_ts, g.M, g.N, g.K, g.c,
-                       g.c_bf16, g.amax);
+    hipLaunchKernelGGL((gemm_nt_kernel<ALIGNED, BF16, QUANT>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, g.a_codes, g.a_scales, g.a_ts, g.b_codes, g.b_scales, g.b_ts, g.M, g.N, g.K,
+                       g.c, g.c_bf16, g.amax, g.q);
 }
 
 void launch_gemm_nt(const GemmArgs& g, hipStream_t stream) {
     const bool aligned = g.K % kBK == 0;
-    if (g.c_bf16) {
-        if (aligned) launch_gemm<true, true>(g, stream);
-        else launch_gemm<false, true>(g, stream);
+    if (g.c_bf16 && g.q.ts) {
+        if (aligned) launch_gemm<true, true, true>(g, stream);
+        else launch_gemm<false, true, true>(g, stream);
+    } else if (g.c_bf16) {
+        if (aligned) launch_gemm<true, true, false>(g, stream);
+        else launch_gemm<false, true, false>(g, stream);
     } else {
-        if (aligned) launch_gemm<true, false>(g, stream);
-        else launch_gemm<false, false>(g, stream);
+        if (aligned) launch_gemm<true, false, false>(g, stream);
+        else launch_gemm<false, false, false>(g, stream);
     }
 }
 

@@ -38,6 +38,20 @@ void launch_zero_scalar(float* p, hipStream_t stream);
 void launch_current_tensor_scale(const float* amax, float* tensor_scale, float max_safe,
                                  hipStream_t stream);
 
+// Block-16 quantization of the GEMM's bf16 output in its epilogue, for the
+// next linear: the stand-alone quantizer's outputs for the M x N output
+// (row-wise along N, transposed along M), tensor scale *ts, nullable pairs.
+struct OutputQuant {
+    const float* ts;
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    uint8_t* col_codes;
+    uint8_t* col_scales;
+    uint64_t seed;
+    uint32_t offset;
+    bool stochastic;
+};
+
 struct GemmArgs {
     const uint8_t* a_codes;
     const uint8_t* a_scales;
@@ -49,6 +63,7 @@ struct GemmArgs {
     float* c;             // fp32 output, or
     uint16_t* c_bf16;     // bf16 output (round to nearest even) ...
     float* amax;          // ... with max|C_bf16| folded into *amax (nullable)
+    OutputQuant q;        // bf16 output only: its block-16 quantization (q.ts null: none)
 };
 
 void launch_gemm_nt(const GemmArgs& g, hipStream_t stream);

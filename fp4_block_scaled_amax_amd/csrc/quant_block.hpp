@@ -1,0 +1,169 @@
+// Block-16 quantization steps shared by the stand-alone quantizer and the
+// GEMM epilogue that quantizes its own output: the block scale of a block
+// amax, the element codes, and the small lane helpers they use.
+//
+// Method: "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining"
+// (arXiv 2609.02846), abstract: E2M1 payloads, one UE5M3 scale per 16
+// elements, fp32 tensor scale.  Per block: s_raw = amax / (6 ts) by the
+// refined division of formats.hpp (equal to IEEE division wherever the code
+// depends on it); the UE5M3 code from the bits of s_raw without branches
+// (normal, subnormal, saturated); r = 1 / (ts * s_b) from a 256-entry table
+// each workgroup builds with IEEE division; round-to-nearest payloads from
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 (equal to the nearest-even
+// definition for every non-NaN fp32 input, checked on gfx950); blocks the
+// fast path cannot take are redone by the definition.
+#pragma once
+
+#include "formats.hpp"
+
+namespace ue5m3fp4 {
+namespace {
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    u16x2_t x, y;
+    __builtin_memcpy(&x, &a, 4);
+    __builtin_memcpy(&y, &b, 4);
+    const u16x2_t m = __builtin_elementwise_max(x, y);
+    uint32_t out;
+    __builtin_memcpy(&out, &m, 4);
+    return out;
+}
+
+// value held by the partner lane (lane ^ 1)
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+struct Ctx {
+    float ts, K, yK;  // K = 6 ts, yK = RN(1 / K)
+    bool fastK;       // K inside the range where the refined division is exact
+    bool tinyOK;      // K >= 1: a block amax below 2^-100 gives scale code 0
+};
+
+struct BlockScale {
+    uint32_t code;  // UE5M3 byte
+    float r;        // RN(1 / (ts * s_b)); 0 for code 0 (payload = sign only)
+};
+
+// Block scale by the definition (any amax, any tensor scale): IEEE division,
+// the integer encoder and decoder.  r is NaN for a NaN block.
+__device__ __noinline__ BlockScale block_scale_general(uint32_t amax16, float ts, float K) {
+    const float amax = __uint_as_float(amax16 << 16);
+    BlockScale b;
+    b.code = ue5m3_encode(amax / K);
+    if (b.code == 0u) b.r = 0.0f;
+    else if (b.code == kUe5m3Nan) b.r = __uint_as_float(0x7FC00000u);
+    else b.r = 1.0f / (ts * ue5m3_decode(b.code));
+    return b;
+}
+
+// Reciprocal table entry for scale code c: RN(1 / RN(ts * s_c)) by IEEE
+// division, 0 for code 0; NaN marks codes the fast path must not use (the
+// NaN code, and reciprocals that overflow or are NaN).
+__device__ __forceinline__ float rcp_entry(uint32_t c, float ts) {
+    if (c == 0u) return 0.0f;
+    if (c == kUe5m3Nan) return __uint_as_float(0x7FC00000u);
+    const float r = 1.0f / (ts * ue5m3_decode(c));
+    return fabsf(r) <= 3.4028235e38f ? r : __uint_as_float(0x7FC00000u);
+}
+
+// Fast block scale.  s = amax / K by the refined division (exact for
+// amax >= 2^-100 and K in [2^-100, 2^100] wherever the code depends on it:
+// quotients below 2^-100 give code 0 and above 2^100 saturate either way).
+// Normal range (s >= 2^-14, or s overflowed to NaN): keep 3 mantissa bits of
+// s, round the other 20 to nearest even, saturate at 0xFE.  Below 2^-14:
+// code = rint(s * 2^17) (0..8; 8 is the smallest normal code).  r comes
+// from the per-workgroup table.  `ok` is cleared for blocks the fast path
+// cannot take (Inf/NaN amax, tiny amax with K < 1, NaN table entries).
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax16, const Ctx& c,
+                                                  const float* __restrict__ rlut, bool& ok) {
+    const float amax = __uint_as_float(amax16 << 16);
+    const float q = amax * c.yK;
+    const float rr = __builtin_fmaf(-c.K, q, amax);
+    const float s = __builtin_fmaf(rr, c.yK, q);
+    const uint32_t sb = __float_as_uint(s);
+    const uint32_t rounded = min((sb + 0x7FFFFu + ((sb >> 20) & 1u)) >> 20, (112u << 3) + kUe5m3MaxCode);
+    // clamped to [0, 8] so the conversion is defined for every s
+    const uint32_t code_s = (uint32_t)fminf(fmaxf(__builtin_rintf(s * 0x1p17f), 0.0f), 8.0f);
+    const uint32_t code_n = (rounded - (112u << 3)) & 0xFFu;
+    const uint32_t sub = s < 0x1p-14f ? ~0u : 0u;
+    BlockScale b;
+    b.code = (code_s & sub) | (code_n & ~sub);
+    b.r = rlut[b.code];
+    ok = ok & (amax16 < 0x7F80u) & ((amax16 >= 0x0D80u) | c.tinyOK) & (b.r == b.r);
+    return b;
+}
+
+// 8 fp32 values -> 8 E2M1 nibbles (element k in nibble k).
+// RNE: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1
+// exactly as the nearest-even definition does, sign included (checked on
+// gfx950 for all 2^32 non-NaN inputs).  SR: magnitude index from formats.hpp.
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rnd) {
+    if (!SR) {
+        uint32_t p = 0u;
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], 1.0f, 0);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], 1.0f, 1);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], 1.0f, 2);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
+        return p;
+    }
+    uint32_t p = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
+        p |= (sign | e2m1_sr_index(fabsf(v[k]), sr_u16(rnd, k))) << (4 * k);
+    }
+    return p;
+}
+
+// Software element codes for blocks from block_scale_general: the same
+// definition with the NaN-block rule (sign only) and any r.  The 8 bf16
+// inputs arrive as 4 words (element 2i in the low half of word i).
+template <bool SR>
+__device__ __noinline__ uint32_t encode8_general(u32x4 w, uint32_t code, float r, U32x4 rnd) {
+    uint32_t p = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t word = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+        const float x = (k & 1) ? bf16_hi(word) : bf16_lo(word);
+        const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+        const float a = fabsf(x * r);
+        const uint32_t idx = SR ? e2m1_sr_index(a, sr_u16(rnd, k)) : e2m1_rne_index(a);
+        p |= (sign | (code == kUe5m3Nan ? 0u : idx)) << (4 * k);
+    }
+    return p;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
+// Per-call constants of the tensor scale ts (a device scalar read once).
+__device__ __forceinline__ Ctx make_ctx(float ts) {
+    Ctx c;
+    c.ts = ts;
+    c.K = 6.0f * ts;
+    c.yK = 1.0f / c.K;
+    c.fastK = c.K >= 0x1p-100f && c.K <= 0x1p100f;
+    c.tinyOK = c.K >= 1.0f;
+    return c;
+}
+
+// Largest bf16 magnitude bits among the 8 elements of a 16-byte unit (a NaN
+// sorts above Inf).
+__device__ __forceinline__ uint32_t max_abs8(u32x4 w) {
+    const uint32_t m = pk_max_u16(pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                                  pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+    return max(m & 0xFFFFu, m >> 16);
+}
+
+}  // namespace
+}  // namespace ue5m3fp4

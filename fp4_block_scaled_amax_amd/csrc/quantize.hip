@@ -25,19 +25,10 @@
 //    bands of 256 rows column by column, so tiles sharing 128-byte lines of
 //    the transposed output meet in one L2.
 //
-// Arithmetic per block: the block amax is an integer max over bf16
-// magnitudes (packed 16-bit max; a NaN sorts above +Inf).  s_raw = amax/(6 ts)
-// uses the refined division of formats.hpp (equal to IEEE division wherever
-// the code depends on it); the UE5M3 code comes from the bits of s_raw
-// without branches (normal, subnormal, saturated); r = 1/(ts * s_b) comes
-// from a 256-entry table each workgroup builds with IEEE division.
-// Round-to-nearest payloads come from v_cvt_scalef32_pk_fp4_f32 with scale
-// 1.0, which rounds an fp32 value to E2M1 exactly as the nearest-even
-// definition does (checked on gfx950 for all 2^32 non-NaN inputs).  Blocks
-// the fast path cannot take (NaN/Inf amax, extreme tensor scales) make the
-// thread redo its blocks by the definition.
+// Arithmetic per block and element: quant_block.hpp.
 #include "formats.hpp"
 #include "kernels.hpp"
+#include "quant_block.hpp"
 
 namespace ue5m3fp4 {
 
@@ -62,25 +53,6 @@ constexpr int kTileCols = 256;
 constexpr int kThreads = 256;
 constexpr int kLdsRowBytes = kTileCols * 2;  // one bf16 tile row
 
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    u16x2_t x, y;
-    __builtin_memcpy(&x, &a, 4);
-    __builtin_memcpy(&y, &b, 4);
-    const u16x2_t m = __builtin_elementwise_max(x, y);
-    uint32_t out;
-    __builtin_memcpy(&out, &m, 4);
-    return out;
-}
-
-// value held by the partner lane (lane ^ 1)
-__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-
 // LDS position of 16-byte unit u (8 columns) of tile row `row`: the unit
 // index is XORed with the row's 16-row block times 16 / kRowBlocks, so the
 // column pass (lanes over kRowBlocks row blocks x kPairsPerWave column pairs)
@@ -89,114 +61,6 @@ template <int TR>
 __device__ __forceinline__ int lds_offset(int row, int u) {
     constexpr int kRowBlocks = Shape<TR>::kRowBlocks;
     return row * kLdsRowBytes + ((u ^ (((row >> 4) & (kRowBlocks - 1)) * (16 / kRowBlocks))) << 4);
-}
-
-struct Ctx {
-    float ts, K, yK;  // K = 6 ts, yK = RN(1 / K)
-    bool fastK;       // K inside the range where the refined division is exact
-    bool tinyOK;      // K >= 1: a block amax below 2^-100 gives scale code 0
-};
-
-struct BlockScale {
-    uint32_t code;  // UE5M3 byte
-    float r;        // RN(1 / (ts * s_b)); 0 for code 0 (payload = sign only)
-};
-
-// Block scale by the definition (any amax, any tensor scale): IEEE division,
-// the integer encoder and decoder.  r is NaN for a NaN block.
-__device__ __noinline__ BlockScale block_scale_general(uint32_t amax16, float ts, float K) {
-    const float amax = __uint_as_float(amax16 << 16);
-    BlockScale b;
-    b.code = ue5m3_encode(amax / K);
-    if (b.code == 0u) b.r = 0.0f;
-    else if (b.code == kUe5m3Nan) b.r = __uint_as_float(0x7FC00000u);
-    else b.r = 1.0f / (ts * ue5m3_decode(b.code));
-    return b;
-}
-
-// Reciprocal table entry for scale code c: RN(1 / RN(ts * s_c)) by IEEE
-// division, 0 for code 0; NaN marks codes the fast path must not use (the
-// NaN code, and reciprocals that overflow or are NaN).
-__device__ __forceinline__ float rcp_entry(uint32_t c, float ts) {
-    if (c == 0u) return 0.0f;
-    if (c == kUe5m3Nan) return __uint_as_float(0x7FC00000u);
-    const float r = 1.0f / (ts * ue5m3_decode(c));
-    return fabsf(r) <= 3.4028235e38f ? r : __uint_as_float(0x7FC00000u);
-}
-
-// Fast block scale.  s = amax / K by the refined division (exact for
-// amax >= 2^-100 and K in [2^-100, 2^100] wherever the code depends on it:
-// quotients below 2^-100 give code 0 and above 2^100 saturate either way).
-// Normal range (s >= 2^-14, or s overflowed to NaN): keep 3 mantissa bits of
-// s, round the other 20 to nearest even, saturate at 0xFE.  Below 2^-14:
-// code = rint(s * 2^17) (0..8; 8 is the smallest normal code).  r comes
-// from the per-workgroup table.  `ok` is cleared for blocks the fast path
-// cannot take (Inf/NaN amax, tiny amax with K < 1, NaN table entries).
-__device__ __forceinline__ BlockScale block_scale(uint32_t amax16, const Ctx& c,
-                                                  const float* __restrict__ rlut, bool& ok) {
-    const float amax = __uint_as_float(amax16 << 16);
-    const float q = amax * c.yK;
-    const float rr = __builtin_fmaf(-c.K, q, amax);
-    const float s = __builtin_fmaf(rr, c.yK, q);
-    const uint32_t sb = __float_as_uint(s);
-    const uint32_t rounded = min((sb + 0x7FFFFu + ((sb >> 20) & 1u)) >> 20, (112u << 3) + kUe5m3MaxCode);
-    // clamped to [0, 8] so the conversion is defined for every s
-    const uint32_t code_s = (uint32_t)fminf(fmaxf(__builtin_rintf(s * 0x1p17f), 0.0f), 8.0f);
-    const uint32_t code_n = (rounded - (112u << 3)) & 0xFFu;
-    const uint32_t sub = s < 0x1p-14f ? ~0u : 0u;
-    BlockScale b;
-    b.code = (code_s & sub) | (code_n & ~sub);
-    b.r = rlut[b.code];
-    ok = ok & (amax16 < 0x7F80u) & ((amax16 >= 0x0D80u) | c.tinyOK) & (b.r == b.r);
-    return b;
-}
-
-// 8 fp32 values -> 8 E2M1 nibbles (element k in nibble k).
-// RNE: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1
-// exactly as the nearest-even definition does, sign included (checked on
-// gfx950 for all 2^32 non-NaN inputs).  SR: magnitude index from formats.hpp.
-template <bool SR>
-__device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rnd) {
-    if (!SR) {
-        uint32_t p = 0u;
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], 1.0f, 0);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], 1.0f, 1);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], 1.0f, 2);
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
-        return p;
-    }
-    uint32_t p = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
-        p |= (sign | e2m1_sr_index(fabsf(v[k]), sr_u16(rnd, k))) << (4 * k);
-    }
-    return p;
-}
-
-// Software element codes for blocks from block_scale_general: the same
-// definition with the NaN-block rule (sign only) and any r.  The 8 bf16
-// inputs arrive as 4 words (element 2i in the low half of word i).
-template <bool SR>
-__device__ __noinline__ uint32_t encode8_general(u32x4 w, uint32_t code, float r, U32x4 rnd) {
-    uint32_t p = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t word = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
-        const float x = (k & 1) ? bf16_hi(word) : bf16_lo(word);
-        const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
-        const float a = fabsf(x * r);
-        const uint32_t idx = SR ? e2m1_sr_index(a, sr_u16(rnd, k)) : e2m1_rne_index(a);
-        p |= (sign | (code == kUe5m3Nan ? 0u : idx)) << (4 * k);
-    }
-    return p;
-}
-
-__device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
-    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
-    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
 // Workgroup id -> tile origin.  Workgroups are dispatched round-robin over

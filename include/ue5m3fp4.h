@@ -182,6 +182,30 @@ UE5M3FP4_API int ue5m3fp4_gemm_nt_bf16(const uint8_t* a_codes, const uint8_t* a_
                           int64_t M, int64_t N, int64_t K, uint16_t* c, float* amax_inout,
                           void* stream);
 
+/* ue5m3fp4_gemm_nt_bf16 whose epilogue also quantizes the bf16 output for
+ * the next linear layer ("format-aware fusion" article in the UFP4 page's
+ * similar-articles list: scale computation and packing fused with the GEMM).
+ * The quantized outputs are exactly those of ue5m3fp4_quantize_blockscale
+ * applied to the bf16 C that this call writes (rows = M, cols = N, ld = N):
+ *   c_row_codes/c_row_scales: [M][N/2], [M][N/16] (blocks along N; N % 16);
+ *   c_col_codes/c_col_scales: [N][M/2], [N][M/16] (C^T, blocks along M;
+ *       M % 16);
+ *   c_tensor_scale: device fp32 scalar, the output's (periodic) tensor scale;
+ *   rounding, seed, offset: as ue5m3fp4_quantize_blockscale (SR streams of
+ *       the M x N output, orientation 0 row-wise and 1 transposed).
+ * Each pair is both NULL or both non-NULL; at least one pair (EINVAL).
+ * amax_inout (nullable) receives max(*amax_inout, max|C|) as in
+ * ue5m3fp4_gemm_nt_bf16 -- the running amax of the next tensor-scale
+ * refresh.  Other rules as ue5m3fp4_gemm_nt_bf16; c and the outputs must not
+ * overlap. */
+UE5M3FP4_API int ue5m3fp4_gemm_nt_bf16_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const float* a_ts, const uint8_t* b_codes,
+                                    const uint8_t* b_scales, const float* b_ts, int64_t M,
+                                    int64_t N, int64_t K, uint16_t* c, float* amax_inout,
+                                    const float* c_tensor_scale, int rounding, uint64_t seed,
+                                    uint32_t offset, uint8_t* c_row_codes, uint8_t* c_row_scales,
+                                    uint8_t* c_col_codes, uint8_t* c_col_scales, void* stream);
+
 /* Native MXFP4 comparison GEMM: the block format gfx950's scaled FP4 MFMA
  * takes natively (OCP Microscaling: E2M1 elements, one E8M0 scale 2^(c-127)
  * per 32 elements, 0xFF = NaN), with the same tensor-scale epilogue as

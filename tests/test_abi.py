@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -145,6 +145,24 @@ def test_gemm_bf16_argument_checks(L):
     assert g(P, P, P, P, P, P, 4, 4, 16, P, P + 2, None) == EALIGN       # amax alignment
     assert g(P, P, P, P, P, P, 1 << 31, 4, 16, P, None, None) == ERANGE
     assert g(None, None, None, None, None, None, 4, 0, 16, None, None, None) == OK  # empty
+
+
+def test_gemm_bf16_quantized_argument_checks(L):
+    def g(M=32, N=32, K=32, c=P, ts=P, rnd=0, rc=P, rs=P, cc=P, cs=P, ac=P):
+        return L.ue5m3fp4_gemm_nt_bf16_quantized(ac, P, P, P, P, P, M, N, K, c, None, ts, rnd, 0, 0,
+                                                 rc, rs, cc, cs, None)
+    assert g(M=-1) == EINVAL
+    assert g(ts=None) == EINVAL
+    assert g(rnd=2) == EINVAL
+    assert g(rc=None) == EINVAL                       # half of a pair
+    assert g(rc=None, rs=None, cc=None, cs=None) == EINVAL  # nothing to quantize
+    assert g(N=40) == ESHAPE                          # row output needs N % 16
+    assert g(M=40) == ESHAPE                          # transposed output needs M % 16
+    assert g(K=24) == ESHAPE                          # K % 16
+    assert g(rc=P + 4) == EALIGN
+    assert g(ts=P + 2) == EALIGN
+    assert g(c=None) == EINVAL
+    assert g(ac=None) == EINVAL
 
 
 def test_gemm_mxfp4_argument_checks(L):
