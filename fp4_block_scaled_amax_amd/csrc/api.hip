@@ -16,6 +16,12 @@ constexpr int64_t kMaxElems = (int64_t)1 << 40;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
+// The runtime's last-error slot is per thread and also holds the errors of
+// earlier, unrelated calls (a caller's failed query, a framework's lazy
+// initialization).  It is cleared right before this library's launches, so
+// that launch_status reports only their own failures.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 int launch_status() {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? UE5M3FP4_OK : UE5M3FP4_EHIP;
@@ -70,6 +76,7 @@ int run_gemm(const uint8_t* ac, const uint8_t* as, const float* at, const uint8_
     if (st != UE5M3FP4_OK) return st;
     if (M == 0 || N == 0) return UE5M3FP4_OK;
     GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, c, nullptr, nullptr};
+    clear_stale_error();
     launch_gemm_nt(g, (hipStream_t)stream);
     return launch_status();
 }
@@ -82,6 +89,7 @@ int run_gemm_bf16(const uint8_t* ac, const uint8_t* as, const float* at, const u
     if (amax && !aligned4(amax)) return UE5M3FP4_EALIGN;
     if (M == 0 || N == 0) return UE5M3FP4_OK;
     GemmArgs g{ac, as, at, bc, bs, bt, M, N, K, nullptr, c, amax, q};
+    clear_stale_error();
     launch_gemm_nt(g, (hipStream_t)stream);
     return launch_status();
 }
@@ -115,6 +123,7 @@ int ue5m3fp4_quantize_blockscale(const uint16_t* x, int64_t rows, int64_t cols, 
     QuantizeArgs a{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
                    seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
                    amax_inout};
+    clear_stale_error();
     launch_quantize_blockscale(a, (hipStream_t)stream);
     return launch_status();
 }
@@ -133,6 +142,7 @@ int ue5m3fp4_quantize_blockscale_2d(const uint16_t* x, int64_t rows, int64_t col
     QuantizeArgs a{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
                    seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
                    amax_inout};
+    clear_stale_error();
     launch_quantize_2d(a, (hipStream_t)stream);
     return launch_status();
 }
@@ -150,6 +160,7 @@ int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t rows, int64_t c
     if (st != UE5M3FP4_OK || rows == 0 || cols == 0) return st;
     const hipStream_t s = (hipStream_t)stream;
     // 1. amax pass over x
+    clear_stale_error();
     launch_zero_scalar(amax_out, s);
     QuantizeArgs pre{x, rows, cols, ld, nullptr, false, 0, 0, nullptr, nullptr, nullptr, nullptr, amax_out};
     launch_quantize_blockscale(pre, s);
@@ -172,6 +183,7 @@ int ue5m3fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float
     if (!codes || !scales || !tensor_scale || !out) return UE5M3FP4_EINVAL;
     if (!aligned16(codes) || !aligned16(scales) || !aligned4(tensor_scale) || !aligned16(out))
         return UE5M3FP4_EALIGN;
+    clear_stale_error();
     launch_dequantize(codes, scales, tensor_scale, rows, cols, out, (hipStream_t)stream);
     return launch_status();
 }
@@ -214,9 +226,11 @@ int ue5m3fp4_gemm_nt_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
     if (st != UE5M3FP4_OK || M == 0 || N == 0) return st;
     GemmArgs g{a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, nullptr, nullptr};
     if (K == 0) {  // an empty sum: the UE5M3 kernel writes the zeros
+        clear_stale_error();
         launch_gemm_nt(g, (hipStream_t)stream);
         return launch_status();
     }
+    clear_stale_error();
     launch_gemm_nt_mx(g, (hipStream_t)stream);
     return launch_status();
 }
@@ -255,6 +269,7 @@ int ue5m3fp4_update_tensor_scale(float* amax_running, float* tensor_scale, int64
     if (!(max_safe > 0.0f) || !std::isfinite(max_safe)) return UE5M3FP4_EINVAL;
     if (!aligned4(amax_running) || !aligned4(tensor_scale)) return UE5M3FP4_EALIGN;
     if (step % period != 0) return UE5M3FP4_OK;
+    clear_stale_error();
     launch_update_tensor_scale(amax_running, tensor_scale, max_safe, (hipStream_t)stream);
     return launch_status();
 }

@@ -274,3 +274,28 @@ def test_amax_only_pass(cuda_device, shape, ld, kind):
     nan_amax = dev_scalar(0.0)
     lib.quantize_blockscale(xd2, None, amax=nan_amax)
     assert np.isnan(host(nan_amax)[0])
+
+
+def test_earlier_runtime_error_is_not_reported(cuda_device):
+    """An error left in the runtime's per-thread last-error slot by an earlier,
+    unrelated call (here a failed hipSetDevice) is not reported as the
+    library's own launch failure."""
+    import ctypes
+
+    import torch
+
+    bits = random_bf16((64, 64), seed=5)
+    ts = fresh_ts(bits)
+    x = dev_bf16(bits)
+    ts_dev = dev_scalar(ts)
+    qr, qc = lib.empty_quantized(64, 64, ts_dev), lib.empty_quantized(64, 64, ts_dev)
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    assert hip.hipSetDevice(1 << 20) != 0  # invalid ordinal: fails, changes nothing
+    st = lib.load_library().ue5m3fp4_quantize_blockscale(
+        x.data_ptr(), 64, 64, 64, ts_dev.data_ptr(), lib.RNE, 0, 0, qr.codes.data_ptr(),
+        qr.scales.data_ptr(), qc.codes.data_ptr(), qc.scales.data_ptr(), None, None)
+    hip.hipGetLastError()  # leave the slot clean for the framework either way
+    assert st == 0, lib.status_string(st)
+    assert_quant_equal(qr, bits, ts, lib.RNE, 0, 0, 0)
+    assert_quant_equal(qc, bits, ts, lib.RNE, 0, 0, 1)
