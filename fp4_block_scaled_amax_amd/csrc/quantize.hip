@@ -24,6 +24,12 @@
 //  - Tile order: each XCD takes a contiguous range of an order that runs down
 //    bands of 256 rows column by column, so tiles sharing 128-byte lines of
 //    the transposed output meet in one L2.
+//  - Cache policy: x is read once, so its loads are non-temporal (streamed
+//    past the caches instead of displacing the partial lines of transposed
+//    codes and scales that neighbouring tiles are still filling in L2), and so
+//    are the row-wise code stores, whose wave stores cover whole lines.  The
+//    partial-line outputs (transposed codes, all scale bytes) stay cached:
+//    written non-temporally they reach HBM unmerged (measured 1.2-2x slower).
 //
 // Arithmetic per block and element: quant_block.hpp.
 #include "formats.hpp"
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(1024) void amax_kernel(const uint16_t* __restrict__
     auto unit_max = [&](int64_t i) __attribute__((always_inline)) {
         const int64_t r = ld == cols ? 0 : i / units_row;
         const int64_t off = ld == cols ? i * 8 : r * ld + (i - r * units_row) * 8;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(x + off);
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
         const uint32_t p = pk_max_u16(pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
                                       pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
         return p;
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
         for (int k = 0; k < kRowsPerThread; ++k) {
             const int64_t r = min(R0 + rbase + 8 * k, rows - 1);
-            w[k] = *reinterpret_cast<const u32x4*>(src + r * ld);
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r * ld));
         }
     }
 
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             // both lanes of a pair store the block's scale byte (same value)
 #pragma unroll
             for (int k = 0; k < kRowsPerThread; ++k) {
-                *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+                __builtin_nontemporal_store(packed[k], reinterpret_cast<uint32_t*>(pc + k * cstep));
                 ps[k * sstep] = (uint8_t)code[k];
             }
         } else {
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t r = min(rb + 2 * k, rows - 1);
-            w[k] = *reinterpret_cast<const u32x4*>(src + r * ld);
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r * ld));
         }
     }
 
@@ -526,7 +532,8 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
         const int k0 = 4 * (u & 1);
         if (interior) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) *reinterpret_cast<uint32_t*>(pc + k * cstep) = packed[k];
+            for (int k = 0; k < 8; ++k)
+                __builtin_nontemporal_store(packed[k], reinterpret_cast<uint32_t*>(pc + k * cstep));
 #pragma unroll
             for (int k = 0; k < 4; ++k) ps[(k0 + k) * sstep] = (uint8_t)b.code;
         } else if (col_ok) {
