@@ -112,11 +112,41 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
         p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
         return p;
     }
+    // Stochastic rounding on v_cvt_scalef32_sr_pk_fp4_f32.  Measured on
+    // gfx950: its first element rounds up iff floor(f * 2^32) + seed >= 2^32,
+    // f being the fraction of |v| between its two E2M1 neighbours (sign
+    // copied, saturation at 6); its second element sees seed << 1, so each
+    // element gets an instruction of its own (the other slot holds +0, which
+    // encodes to 0 whatever the seed).  With seed = ~(u << 16) =
+    // (65535 - u) * 2^16 + 65535 that is "round up iff f * 2^32 > u * 2^16",
+    // i.e. u < 65536 f, the definition -- exactly wherever f * 2^32 is an
+    // integer, which holds for |v| >= 2^-10.  Elements below 2^-9 (rare:
+    // far below their block's largest) are redone by the definition.  Only
+    // byte 0 of the instruction's result is defined here.
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
     uint32_t p = 0u;
+    uint32_t tiny = 0u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
-        p |= (sign | e2m1_sr_index(fabsf(v[k]), sr_u16(rnd, k))) << (4 * k);
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w = rnd.v[j];  // u of element 2j in the low half, of 2j + 1 in the high half
+        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{v[2 * j], 0.0f}, ~(w << 16),
+                                                                         1.0f, 0);
+        const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
+            0u, f32x2_t{v[2 * j + 1], 0.0f}, ~(w & 0xFFFF0000u), 1.0f, 0);
+        p |= ((lo & 0xFu) | ((hi & 0xFu) << 4)) << (8 * j);
+        tiny |= (fabsf(v[2 * j]) < 0x1p-9f ? 1u : 0u) << (2 * j);
+        tiny |= (fabsf(v[2 * j + 1]) < 0x1p-9f ? 1u : 0u) << (2 * j + 1);
+    }
+    if (__builtin_expect(tiny != 0u, 0)) {
+        // |v| < 2^-9 < 0.5: the neighbours are 0 and 0.5 and 65536 f = |v| * 2^17
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if ((tiny >> k) & 1u) {
+                const uint32_t up = (float)sr_u16(rnd, k) < fabsf(v[k]) * 0x1p17f ? 1u : 0u;
+                const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
+                p = (p & ~(0xFu << (4 * k))) | ((sign | up) << (4 * k));
+            }
+        }
     }
     return p;
 }

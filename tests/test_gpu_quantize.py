@@ -11,7 +11,7 @@ import pytest
 
 import fp4_block_scaled_amax_amd as lib
 from oracle import formats, quantize, tensor_scale
-from workloads import config, random_bf16, sr_seed, STALE_FACTORS
+from workloads import config, random_bf16, sr_seed, to_bf16_bits, STALE_FACTORS
 
 from devhelpers import (assert_quant_equal, dev_bf16, dev_scalar, fresh_ts, gpu_quantize, host,
                         sample_rows)
@@ -299,3 +299,23 @@ def test_earlier_runtime_error_is_not_reported(cuda_device):
     assert st == 0, lib.status_string(st)
     assert_quant_equal(qr, bits, ts, lib.RNE, 0, 0, 0)
     assert_quant_equal(qc, bits, ts, lib.RNE, 0, 0, 1)
+
+
+@pytest.mark.parametrize("seed", [1, 77, 2**40 + 3])
+def test_sr_every_magnitude_class(cuda_device, seed):
+    """Stochastic rounding over scaled magnitudes from 6 down to 2^-24 (every
+    E2M1 interval, the sub-2^-9 range, values on and next to grid points),
+    both orientations, several random streams: bit-exact with the oracle."""
+    rng = np.random.default_rng(seed % 1000)
+    R, C = 128, 512
+    u = rng.uniform(-24.0, 0.0, size=(R, C))
+    x = np.sign(rng.standard_normal((R, C))) * np.exp2(u)
+    x[:, ::16] = 1.0                                   # every row block: amax 1
+    grid = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0]) / 6.0
+    x[::3, 5::16] = rng.choice(grid, size=x[::3, 5::16].shape)  # near grid points
+    bits = to_bf16_bits(x.astype(np.float32))
+    ts = np.float32(1.0 / 6.0)  # scale 1: v = 6 x within row blocks
+    for offset in (0, 5):
+        qr, qc = gpu_quantize(dev_bf16(bits), ts, lib.SR, seed=seed, offset=offset)
+        assert_quant_equal(qr, bits, ts, lib.SR, seed, offset, 0)
+        assert_quant_equal(qc, bits, ts, lib.SR, seed, offset, 1)
