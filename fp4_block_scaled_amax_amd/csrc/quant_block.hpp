@@ -120,7 +120,7 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
     // encodes to 0 whatever the seed).  With seed = ~(u << 16) =
     // (65535 - u) * 2^16 + 65535 that is "round up iff f * 2^32 > u * 2^16",
     // i.e. u < 65536 f, the definition -- exactly wherever f * 2^32 is an
-    // integer, which holds for |v| >= 2^-10.  Elements below 2^-9 (rare:
+    // integer, which holds for |v| >= 2^-10.  Elements below 2^-10 (rare:
     // far below their block's largest) are redone by the definition.  Only
     // byte 0 of the instruction's result is defined here.
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -134,11 +134,11 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
         const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
             0u, f32x2_t{v[2 * j + 1], 0.0f}, ~(w & 0xFFFF0000u), 1.0f, 0);
         p |= ((lo & 0xFu) | ((hi & 0xFu) << 4)) << (8 * j);
-        tiny |= (fabsf(v[2 * j]) < 0x1p-9f ? 1u : 0u) << (2 * j);
-        tiny |= (fabsf(v[2 * j + 1]) < 0x1p-9f ? 1u : 0u) << (2 * j + 1);
+        tiny |= (fabsf(v[2 * j]) < 0x1p-10f ? 1u : 0u) << (2 * j);
+        tiny |= (fabsf(v[2 * j + 1]) < 0x1p-10f ? 1u : 0u) << (2 * j + 1);
     }
     if (__builtin_expect(tiny != 0u, 0)) {
-        // |v| < 2^-9 < 0.5: the neighbours are 0 and 0.5 and 65536 f = |v| * 2^17
+        // |v| < 2^-10 < 0.5: the neighbours are 0 and 0.5 and 65536 f = |v| * 2^17
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             if ((tiny >> k) & 1u) {

@@ -41,10 +41,9 @@ namespace ue5m3fp4 {
 namespace {
 
 // Tile shape: TR (32 or 64) rows x 256 columns per 256-thread workgroup.
-// Stochastic rounding and row-only calls use 32-row tiles (more resident
-// workgroups hide more of the Philox and load latency); round-to-nearest
-// calls with the transposed output use 64-row tiles (32-byte runs of
-// transposed codes per column instead of 16).
+// Row-only calls use 32-row tiles (more resident workgroups hide more load
+// latency); calls with the transposed output use 64-row tiles (32-byte runs
+// of transposed codes per column instead of 16).
 template <int TR>
 struct Shape {
     static constexpr int kTileRows = TR;
@@ -369,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
 template <bool ROW, bool COL, bool SR, bool AMAX>
 void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
-    constexpr int TR = (COL && !SR) ? 64 : 32;
+    constexpr int TR = COL ? 64 : 32;
     const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + TR - 1) / TR);
     hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
                        a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
