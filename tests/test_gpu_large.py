@@ -1,0 +1,104 @@
+"""Maximum-size edge cases: tensors past 2^31 elements and GEMM outputs past
+2^31 entries, so every byte offset needs 64 bits.  Inputs are generated on
+the device from a seeded generator; sampled rows / entries are compared with
+the oracle (round to nearest: the codes do not depend on coordinates, so a
+sampled row can be quantized on its own).
+
+Sizes: x is 133120 x 16384 bf16 (2.18e9 elements, 4.4 GB; outputs 1.2 GB per
+orientation); C is 65536 x 36864 fp32 (2.4e9 entries, 9.7 GB)."""
+
+import numpy as np
+import pytest
+
+import fp4_block_scaled_amax_amd as lib
+from oracle import quantize, quantize2d
+
+from devhelpers import dev_scalar, host
+
+pytestmark = pytest.mark.gpu
+
+R, C = 133120, 16384
+ROWS = [0, 1, 8191, 65535, 65536, 131071, R - 16, R - 1]
+COLS = [0, 7, 4096, C - 1]
+
+
+@pytest.fixture(scope="module")
+def big_x(cuda_device):
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(20260)
+    x = torch.randn((R, C), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    assert x.numel() > 2**31
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    import torch
+
+    return host(t.contiguous().view(torch.int16)).view(np.uint16)
+
+
+def test_quantize_past_2_31_elements(big_x):
+    import torch
+
+    ts_val = np.float32(float(big_x.abs().max().float()) / 43008.0)
+    ts = dev_scalar(ts_val)
+    amax = dev_scalar(0.0)
+    qr = lib.empty_quantized(R, C, ts)
+    qc = lib.empty_quantized(C, R, ts)
+    lib.quantize_blockscale(big_x, ts, lib.RNE, row=qr, col=qc, amax=amax)
+    torch.cuda.synchronize()
+    assert host(amax)[0] == np.float32(big_x.abs().max().float().item())
+    xr = _bits(big_x[ROWS])
+    c, s = quantize.quantize_blockscale(xr, ts_val, quantize.RNE)
+    assert np.array_equal(host(qr.codes[ROWS]), c) and np.array_equal(host(qr.scales[ROWS]), s)
+    xc = _bits(big_x[:, COLS])  # R x k: output rows of the transposed orientation
+    c, s = quantize.quantize_blockscale(xc, ts_val, quantize.RNE, orientation=1)
+    assert np.array_equal(host(qc.codes[COLS]), c) and np.array_equal(host(qc.scales[COLS]), s)
+    del qr, qc
+
+
+def test_quantize_2d_past_2_31_elements(big_x):
+    import torch
+
+    ts_val = np.float32(float(big_x.abs().max().float()) / 43008.0)
+    ts = dev_scalar(ts_val)
+    qr = lib.empty_quantized(R, C, ts)
+    qc = lib.empty_quantized(C, R, ts)
+    lib.quantize_blockscale_2d(big_x, ts, lib.RNE, row=qr, col=qc)
+    torch.cuda.synchronize()
+    for g in (0, 4096, R // 16 - 1):  # 16-row groups
+        xs = _bits(big_x[16 * g:16 * g + 16])
+        rc, rs, cc, cs, _ = quantize2d.quantize_blockscale_2d(xs, ts_val, quantize.RNE)
+        assert np.array_equal(host(qr.codes[16 * g:16 * g + 16]), rc)
+        assert np.array_equal(host(qr.scales[16 * g:16 * g + 16]), rs)
+        assert np.array_equal(host(qc.codes[:, 8 * g:8 * g + 8]), cc)
+        assert np.array_equal(host(qc.scales[:, g:g + 1]), cs)
+    del qr, qc
+
+
+def test_gemm_output_past_2_31_entries(cuda_device):
+    import torch
+
+    M, N, K = 65536, 36864, 32
+    rng = np.random.default_rng(9)
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    asc = rng.integers(0x60, 0x90, size=(M, K // 16), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    bsc = rng.integers(0x60, 0x90, size=(N, K // 16), dtype=np.uint8)
+    a = lib.Quantized(torch.from_numpy(ac).cuda(), torch.from_numpy(asc).cuda(), dev_scalar(0.5))
+    b = lib.Quantized(torch.from_numpy(bc).cuda(), torch.from_numpy(bsc).cuda(), dev_scalar(0.25))
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    assert c.numel() > 2**31
+    lib.gemm_nt(a, b, c)
+    rows = np.array([0, 1, 30000, 58254, 65535, 65535, 40000, 65535])
+    cols = np.array([0, 36863, 17, 36000, 0, 36863, 12345, 36000])
+    got = host(c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+    from oracle import gemm as ogemm
+
+    ref, bound = ogemm.gemm_nt_entries(ac, asc, 0.5, bc, bsc, 0.25, rows, cols)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-5 * bound)
+    del c
+    torch.cuda.empty_cache()
