@@ -162,14 +162,14 @@ int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t rows, int64_t c
     // 1. amax pass over x
     clear_stale_error();
     launch_zero_scalar(amax_out, s);
-    QuantizeArgs pre{x, rows, cols, ld, nullptr, false, 0, 0, nullptr, nullptr, nullptr, nullptr, amax_out};
+    QuantizeArgs pre{x, rows, cols, ld, nullptr, false, 0, 0, nullptr, nullptr, nullptr, nullptr, amax_out,
+                     nullptr, 0.0f};
     launch_quantize_blockscale(pre, s);
-    // 2. the tensor scale of this tensor
-    launch_current_tensor_scale(amax_out, tensor_scale, max_safe, s);
-    // 3. block quantization with it (the amax is already known)
+    // 2. block quantization under this tensor's own scale, which the
+    //    quantizer derives from the amax (and stores to *tensor_scale)
     QuantizeArgs q{x,         rows,      cols,      ld,        tensor_scale, rounding == UE5M3FP4_SR,
                    seed,      offset,    row_codes, row_scales, col_codes,   col_scales,
-                   nullptr};
+                   nullptr,   amax_out,  max_safe};
     launch_quantize_blockscale(q, s);
     return launch_status();
 }

@@ -19,6 +19,11 @@ struct QuantizeArgs {
     uint8_t* col_codes;
     uint8_t* col_scales;
     float* amax_inout;
+    // current-tensor scaling (1-D quantizer only): tensor_scale becomes
+    // fp32(*current_amax / fp32(6 max_safe)) when that amax is finite and > 0
+    // (stored back to *tensor_scale); null for the periodic tensor scale
+    const float* current_amax;
+    float max_safe;
 };
 
 void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t stream);
@@ -32,11 +37,8 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float*
 void launch_update_tensor_scale(float* amax_running, float* tensor_scale, float max_safe,
                                 hipStream_t stream);
 
-// Current-tensor scaling: *amax = 0 (before an amax pass) and
-// *tensor_scale = amax / (6 max_safe) when finite and > 0 (amax kept).
+// *p = 0 (the running amax before a current-tensor-scaling amax pass).
 void launch_zero_scalar(float* p, hipStream_t stream);
-void launch_current_tensor_scale(const float* amax, float* tensor_scale, float max_safe,
-                                 hipStream_t stream);
 
 // Block-16 quantization of the GEMM's bf16 output in its epilogue, for the
 // next linear: the stand-alone quantizer's outputs for the M x N output

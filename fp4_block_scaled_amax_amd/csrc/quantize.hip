@@ -148,13 +148,19 @@ __global__ __launch_bounds__(1024) void amax_kernel(const uint16_t* __restrict__
     amax_commit(m, amax);
 }
 
+// current_amax (nullable): current-tensor scaling -- the tensor scale is
+// fp32(amax / fp32(6 max_safe)) of this tensor's amax (from the amax pass
+// before), or *tensor_scale as passed when that amax is 0 or not finite, and
+// workgroup 0 stores it to *tensor_scale.  Every workgroup computes the same
+// value, and one that reads *tensor_scale after the store reads it only in
+// the case where the store wrote back the value it found.
 template <int TR, bool ROW, bool COL, bool SR, bool AMAX>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-    const float* __restrict__ tensor_scale, uint64_t seed, uint32_t offset,
+    float* tensor_scale, uint64_t seed, uint32_t offset,
     uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
     uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
-    float* __restrict__ amax_inout) {
+    float* __restrict__ amax_inout, const float* __restrict__ current_amax, float max_safe) {
     using S = Shape<TR>;
     constexpr int kTileRows = S::kTileRows, kRowsPerThread = S::kRowsPerThread,
                   kRowBlocks = S::kRowBlocks, kPairsPerWave = S::kPairsPerWave,
@@ -190,6 +196,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     Ctx ctx{0.0f, 0.0f, 0.0f, false, false};
     if (ROW || COL) {
         ctx.ts = *tensor_scale;
+        if (current_amax != nullptr) {
+            const float a = *current_amax;
+            if ((__float_as_uint(a) & 0x7F800000u) != 0x7F800000u && a > 0.0f) ctx.ts = a / (6.0f * max_safe);
+            if (blockIdx.x == 0 && t == 0) *tensor_scale = ctx.ts;
+        }
         ctx.K = 6.0f * ctx.ts;
         ctx.yK = 1.0f / ctx.K;
         ctx.fastK = ctx.K >= 0x1p-100f && ctx.K <= 0x1p100f;
@@ -371,8 +382,8 @@ void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
     constexpr int TR = COL ? 64 : 32;
     const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + TR - 1) / TR);
     hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
-                       a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
-                       a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
+                       a.rows, a.cols, a.ld, const_cast<float*>(a.tensor_scale), a.seed, a.offset, a.row_codes,
+                       a.row_scales, a.col_codes, a.col_scales, a.amax_inout, a.current_amax, a.max_safe);
 }
 
 // Compute units of the current device (the runtime caches the attribute).
@@ -654,26 +665,10 @@ __global__ void zero_scalar_kernel(float* __restrict__ p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
 }
 
-// ts = amax / (6 max_safe) from the current tensor's amax, which is kept;
-// a zero or non-finite amax leaves ts unchanged.
-__global__ void current_tensor_scale_kernel(const float* __restrict__ amax,
-                                            float* __restrict__ tensor_scale, float max_safe) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    const float a = *amax;
-    const uint32_t b = __float_as_uint(a);
-    if ((b & 0x7F800000u) != 0x7F800000u && a > 0.0f) *tensor_scale = a / (6.0f * max_safe);
-}
-
 }  // namespace
 
 void launch_zero_scalar(float* p, hipStream_t s) {
     hipLaunchKernelGGL(zero_scalar_kernel, dim3(1), dim3(64), 0, s, p);
-}
-
-void launch_current_tensor_scale(const float* amax, float* tensor_scale, float max_safe,
-                                 hipStream_t s) {
-    hipLaunchKernelGGL(current_tensor_scale_kernel, dim3(1), dim3(64), 0, s, amax, tensor_scale,
-                       max_safe);
 }
 
 void launch_quantize_blockscale(const QuantizeArgs& a, hipStream_t s) {
