@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantize-only", action="store_true",
                    help="skip the stand-alone quantizer measurement")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip timing the step captured as one HIP graph")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the epilogue-fusion and native-MXFP4 comparisons")
     p.add_argument("--copy-calibration", action="store_true",
@@ -251,6 +253,8 @@ def main():
                      "rne": q_stats(lib.RNE), "sr": q_stats(lib.SR)},
     }
     step_elems = sum(t.elems for t in tensors)
+    if not args.no_graph:
+        result["graph"] = graph_replay(torch, step, args, step_flops)
     if not args.no_extras:
         result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
         result["native_mxfp4"] = native_mxfp4(lib, torch, gemm_tflops)
@@ -261,6 +265,31 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step_flops, step_elems)
     print(json.dumps(result), flush=True)
+
+
+def graph_replay(torch, step, args, step_flops):
+    """The same step captured once as a HIP graph (torch.cuda.graph) and
+    replayed `steps` times: what the step costs without per-launch host work.
+    The captured step keeps one step's stochastic-rounding offsets and refresh
+    decision; its outputs equal the eager step's (tests/test_gpu_graph.py)."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step(args.warmup + args.steps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        del g
+        return {"ms_per_step": round(ms, 4), "value": round(step_flops / (ms * 1e-3) / 1e12, 2)}
+    except Exception as ex:  # capture unsupported by this runtime: report, do not fail the run
+        return f"unavailable: {type(ex).__name__}: {ex}"[:200]
 
 
 def epilogue_fusion(lib, torch, up):
