@@ -211,39 +211,85 @@ __device__ __forceinline__ int qtile_offset(int row, int col) {
 
 // Row-wise block-16 quantization of the bf16 output tile held in LDS
 // (blocks along N): thread t takes 16-byte unit t % 32 of tile rows
-// t / 32 + 8k; the lane pair (t, t ^ 1) shares a block.  Output row m0 + row
-// of the M x N output, stochastic bits from orientation 0 of that shape.
+// t / 32 + 8k, eight rows per batch.  The lane pair (t, t ^ 1) shares a
+// block: lane parity p computes the block scales of the batch's rows 2m + p
+// and the pair swaps them (DPP), as in the stand-alone quantizer.  The
+// batch's LDS reads issue together, and the path check is once per batch.
+// Output row m0 + row of the M x N output, stochastic bits from orientation
+// 0 of that shape.
 template <bool SR>
 __device__ __forceinline__ void quantize_tile_rows(const uint8_t* tile, const Ctx& ctx, const float* rlut,
                                                    const OutputQuant& q, int64_t m0, int64_t n0,
                                                    int64_t M, int64_t N) {
     const int t = threadIdx.x, u = t & 31;
+    const uint32_t p = t & 1;
     const int64_t gc = n0 + 8 * u;
-#pragma unroll 8
-    for (int k = 0; k < kBM / 8; ++k) {
-        const int row = (t >> 5) + 8 * k;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + qtile_offset(row, 8 * u));
-        const uint32_t m = max_abs8(w);
-        const uint32_t amax16 = max(m, swap_pair(m));  // both lanes of the block agree
-        bool ok = ctx.fastK;
-        BlockScale b = block_scale(amax16, ctx, rlut, ok);
-        const int64_t gr = m0 + row;
-        U32x4 rnd;
-        if (SR) rnd = sr_words(((uint64_t)gr * (uint64_t)N + (uint64_t)gc) >> 3, q.offset, 0u, q.seed);
-        uint32_t packed;
-        if (__builtin_expect(ok, 1)) {
-            float v[8];
-            unpack8(w, v);
+#pragma unroll 1
+    for (int batch = 0; batch < kBM / 64; ++batch) {
+        u32x4 w[8];
+        uint32_t hmax[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = v[e] * b.r;
-            packed = encode8<SR>(v, rnd);
-        } else {
-            b = block_scale_general(amax16, ctx.ts, ctx.K);
-            packed = encode8_general<SR>(w, b.code, b.r, rnd);
+        for (int k = 0; k < 8; ++k) {
+            const int row = (t >> 5) + 8 * (8 * batch + k);
+            w[k] = *reinterpret_cast<const u32x4*>(tile + qtile_offset(row, 8 * u));
         }
-        if (gr < M && gc < N) {
-            *reinterpret_cast<uint32_t*>(q.row_codes + gr * (N / 2) + gc / 2) = packed;
-            if ((u & 1) == 0) q.row_scales[gr * (N / 16) + gc / 16] = (uint8_t)b.code;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) hmax[k] = max_abs8(w[k]);
+        uint32_t code[8];
+        float rr[8];
+        bool ok = ctx.fastK;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t mine = p ? hmax[2 * m + 1] : hmax[2 * m];
+            const uint32_t other = p ? hmax[2 * m] : hmax[2 * m + 1];
+            const BlockScale own = block_scale(max(mine, swap_pair(other)), ctx, rlut, ok);
+            const uint32_t pc = swap_pair(own.code);
+            const float pr = __uint_as_float(swap_pair(__float_as_uint(own.r)));
+            code[2 * m] = p ? pc : own.code;
+            rr[2 * m] = p ? pr : own.r;
+            code[2 * m + 1] = p ? own.code : pc;
+            rr[2 * m + 1] = p ? own.r : pr;
+        }
+        // both lanes of the pair take the same path; the exchange runs in
+        // every lane
+        const uint32_t ok_bit = ok ? 1u : 0u;
+        const bool pair_ok = (ok_bit & swap_pair(ok_bit)) != 0u;
+        uint32_t packed[8];
+        if (__builtin_expect(pair_ok, 1)) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float v[8];
+                unpack8(w[k], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = v[e] * rr[k];
+                U32x4 rnd;
+                if (SR) {
+                    const int64_t gr = m0 + (t >> 5) + 8 * (8 * batch + k);
+                    rnd = sr_words(((uint64_t)gr * (uint64_t)N + (uint64_t)gc) >> 3, q.offset, 0u, q.seed);
+                }
+                packed[k] = encode8<SR>(v, rnd);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t blk = max(hmax[k], swap_pair(hmax[k]));  // both lanes active here
+                const BlockScale b = block_scale_general(blk, ctx.ts, ctx.K);
+                U32x4 rnd;
+                if (SR) {
+                    const int64_t gr = m0 + (t >> 5) + 8 * (8 * batch + k);
+                    rnd = sr_words(((uint64_t)gr * (uint64_t)N + (uint64_t)gc) >> 3, q.offset, 0u, q.seed);
+                }
+                packed[k] = encode8_general<SR>(w[k], b.code, b.r, rnd);
+                code[k] = b.code;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t gr = m0 + (t >> 5) + 8 * (8 * batch + k);
+            if (gr < M && gc < N) {
+                *reinterpret_cast<uint32_t*>(q.row_codes + gr * (N / 2) + gc / 2) = packed[k];
+                if (p == 0) q.row_scales[gr * (N / 16) + gc / 16] = (uint8_t)code[k];
+            }
         }
     }
 }
