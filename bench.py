@@ -258,6 +258,7 @@ def main():
     if not args.no_extras:
         result["epilogue_fusion"] = epilogue_fusion(lib, torch, layers[0])
         result["native_mxfp4"] = native_mxfp4(lib, torch, gemm_tflops)
+        result["dynamic_range_stress"] = dynamic_range_stress(lib, torch)
     del layers, tensors
     torch.cuda.empty_cache()
     if not args.no_quantize_only:
@@ -376,6 +377,44 @@ def native_mxfp4(lib, torch, ue5m3_tflops):
         res["vendor_mxfp4_bf16_out"] = {"ms": round(ms_v, 4), "tflops": round(flop / (ms_v * 1e-3) / 1e12, 1)}
     except Exception as ex:  # pragma: no cover
         res["vendor_mxfp4_bf16_out"] = f"unavailable: {type(ex).__name__}"
+    return res
+
+
+def dynamic_range_stress(lib, torch):
+    """The dynamic-range stress tensors (4096 x 4096, magnitudes log-uniform
+    over 2^-24..2^12 per row block) quantized row-wise under a fresh tensor
+    scale and under scales from an amax off by x8 and x1/8 (a stale periodic
+    scale): fraction of blocks flushed to scale 0 although non-zero, of
+    blocks with a subnormal UE5M3 scale, of saturated (0xFE) blocks, and the
+    relative L2 error of the dequantized tensor.  X with round to nearest,
+    dY with stochastic rounding."""
+    from workloads import STALE_FACTORS, config, sr_seed
+
+    data = config(5)
+    res = {"workload": "4096x4096, log-uniform block magnitudes 2^-24..2^12"}
+    for name, rnd in (("X", lib.RNE), ("dY", lib.SR)):
+        x = torch.from_numpy(data[name].view("int16")).cuda()
+        xf = x.view(torch.bfloat16).float()
+        R, C = xf.shape
+        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        lib.quantize_blockscale(x, None, amax=amax)
+        blk_nonzero = xf.abs().view(R, C // 16, 16).amax(dim=2) > 0
+        out = torch.empty((R, C), dtype=torch.float32, device="cuda")
+        entry = {}
+        for label, factor in [("fresh", 1.0)] + [(f"stale_x{f:g}", f) for f in STALE_FACTORS]:
+            ts = (amax * factor / 43008.0).float()
+            q = lib.empty_quantized(R, C, ts)
+            lib.quantize_blockscale(x, ts, rnd, sr_seed(5), 0, row=q)
+            lib.dequantize(q, out)
+            sc = q.scales
+            err = torch.linalg.vector_norm(out - xf) / torch.linalg.vector_norm(xf)
+            entry[label] = {
+                "flushed_frac": round(float(((sc == 0) & blk_nonzero).float().mean()), 5),
+                "subnormal_scale_frac": round(float(((sc > 0) & (sc < 8)).float().mean()), 5),
+                "saturated_frac": round(float((sc == 0xFE).float().mean()), 6),
+                "rel_l2_error": round(float(err), 5),
+            }
+        res[name] = entry
     return res
 
 
