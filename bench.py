@@ -67,22 +67,21 @@ def parse():
 
 
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_nt_kernel_ffn_pair_counters.json")
-GEMM_SOURCE = os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "gemm.hip")
 
 
 def gemm_traffic():
     """HBM bytes per GEMM launch from the committed counter summary, or None
-    when the GEMM source changed since the counters were taken."""
-    import hashlib
+    when the GEMM kernel (its source or its compile options) changed since
+    the counters were taken."""
+    from fp4_block_scaled_amax_amd.build import kernel_fingerprint
 
     try:
         with open(PROFILE_COUNTERS) as f:
             prof = json.load(f)
-        with open(GEMM_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_fingerprint("gemm.hip")
     except (OSError, ValueError):
         return None
-    if prof.get("gemm_source_sha256") != digest:
+    if prof.get("gemm_kernel_fingerprint") != digest:
         return None
     return float(prof["hbm_bytes_per_launch"])
 

@@ -25,6 +25,30 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source code-generation options.  The GEMMs' main loops are long
+# straight-line blocks of MFMAs interleaved with dequantization (or operand
+# moves), LDS and global-load instructions; LLVM's iterative ILP scheduling
+# strategy orders them measurably better than the default on MI355X (about
+# 6 % for the block-scaled GEMM, 11 % for the MXFP4 one at 8192 x 4096 x
+# 16384).  The quantizer gains nothing from it.
+SOURCE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "gemm_mx.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
+def kernel_fingerprint(src):
+    """SHA-256 of a source file and the options it is compiled with: what a
+    recorded measurement of its kernels refers to."""
+    import hashlib
+
+    h = hashlib.sha256()
+    with open(os.path.join(CSRC, src), "rb") as f:
+        h.update(f.read())
+    h.update(repr((HIP_FLAGS, SOURCE_FLAGS.get(src, []))).encode())
+    return h.hexdigest()
+
+
 def hipcc():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +63,7 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)  # the host pass ignores the GPU feature
