@@ -125,7 +125,6 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
     // byte 0 of the instruction's result is defined here.
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     uint32_t p = 0u;
-    uint32_t tiny = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t w = rnd.v[j];  // u of element 2j in the low half, of 2j + 1 in the high half
@@ -134,14 +133,15 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
         const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
             0u, f32x2_t{v[2 * j + 1], 0.0f}, ~(w & 0xFFFF0000u), 1.0f, 0);
         p |= ((lo & 0xFu) | ((hi & 0xFu) << 4)) << (8 * j);
-        tiny |= (fabsf(v[2 * j]) < 0x1p-10f ? 1u : 0u) << (2 * j);
-        tiny |= (fabsf(v[2 * j + 1]) < 0x1p-10f ? 1u : 0u) << (2 * j + 1);
     }
-    if (__builtin_expect(tiny != 0u, 0)) {
+    // one test per 8 elements (v is finite here): the smallest magnitude
+    const float mn = fminf(fminf(fminf(fabsf(v[0]), fabsf(v[1])), fminf(fabsf(v[2]), fabsf(v[3]))),
+                           fminf(fminf(fabsf(v[4]), fabsf(v[5])), fminf(fabsf(v[6]), fabsf(v[7]))));
+    if (__builtin_expect(mn < 0x1p-10f, 0)) {
         // |v| < 2^-10 < 0.5: the neighbours are 0 and 0.5 and 65536 f = |v| * 2^17
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if ((tiny >> k) & 1u) {
+            if (fabsf(v[k]) < 0x1p-10f) {
                 const uint32_t up = (float)sr_u16(rnd, k) < fabsf(v[k]) * 0x1p17f ? 1u : 0u;
                 const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
                 p = (p & ~(0xFu << (4 * k))) | ((sign | up) << (4 * k));

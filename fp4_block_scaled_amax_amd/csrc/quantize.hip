@@ -193,6 +193,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         }
     }
 
+    // Random words of the row-wise output (stochastic rounding): they depend
+    // on coordinates only.  Row-only calls draw them here, while the loads are
+    // in flight; with the transposed output as well, the 32 registers they
+    // would hold meanwhile cost a resident workgroup, so they are drawn where
+    // they are used.
+    auto row_words = [&](int k) {
+        return sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+    };
+    constexpr bool kEarlyWords = SR && ROW && !COL;
+    U32x4 early[kEarlyWords ? kRowsPerThread : 1];
+    if constexpr (kEarlyWords) {
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k) early[k] = row_words(k);
+    }
+
     Ctx ctx{0.0f, 0.0f, 0.0f, false, false};
     if (ROW || COL) {
         ctx.ts = *tensor_scale;
@@ -262,8 +277,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = v[e] * rr[k];
                 U32x4 rnd;
-                if (SR) rnd = sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3,
-                                       offset, 0u, seed);
+                if constexpr (kEarlyWords) rnd = early[k];
+                else if (SR) rnd = row_words(k);
                 packed[k] = encode8<SR>(v, rnd);
             }
         } else {
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
                 const uint32_t blk = max(hmax[k], swap_pair(hmax[k]));  // both lanes active here
                 const BlockScale b = block_scale_general(blk, ctx.ts, ctx.K);
                 U32x4 rnd;
-                if (SR) rnd = sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3,
-                                       offset, 0u, seed);
+                if constexpr (kEarlyWords) rnd = early[k];
+                else if (SR) rnd = row_words(k);
                 packed[k] = encode8_general<SR>(w[k], b.code, b.r, rnd);
                 code[k] = b.code;
             }
