@@ -34,7 +34,8 @@ int check_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
     if (rows < 0 || cols < 0 || ld < 0) return UE5M3FP4_EINVAL;
     if (rounding != UE5M3FP4_RNE && rounding != UE5M3FP4_SR) return UE5M3FP4_EINVAL;
     if (cols % 16 != 0) return UE5M3FP4_ESHAPE;
-    if (rows >= kMaxDim || cols >= kMaxDim || rows * ld >= kMaxElems) return UE5M3FP4_ERANGE;
+    if (rows >= kMaxDim || cols >= kMaxDim || ld >= kMaxElems) return UE5M3FP4_ERANGE;
+    if (ld > 0 && rows > (kMaxElems - 1) / ld) return UE5M3FP4_ERANGE;  // rows * ld >= 2^40, unmultiplied
     if (rows == 0 || cols == 0) return UE5M3FP4_OK;  // empty tensor: nothing to do
     const bool row = row_codes || row_scales;
     const bool col = col_codes || col_scales;

@@ -69,6 +69,9 @@ def test_quantize_argument_checks(L):
     assert q(L, rc=P + 4) == EALIGN
     assert q(L, ts=P + 2) == EALIGN
     assert q(L, rows=1 << 31) == ERANGE
+    assert q(L, rows=1 << 20, ld=1 << 20) == ERANGE   # rows * ld = 2^40
+    assert q(L, rows=(1 << 31) - 1, ld=1 << 39) == ERANGE  # a product past 2^63 must not wrap
+    assert q(L, ld=1 << 62) == ERANGE
     # empty tensors are valid no-ops and touch nothing (even NULL pointers)
     assert q(L, rows=0, x=None, rc=None, rs=None, cc=None, cs=None) == OK
     assert q(L, cols=0, ld=0, x=None) == OK
