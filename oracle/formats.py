@@ -139,3 +139,17 @@ def bf16_to_f32(bits):
     """bfloat16 bit patterns (uint16) -> float32, exactly (bits << 16)."""
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_rne(x):
+    """float32 value(s) -> bfloat16 bit patterns (uint16), round to nearest
+    with ties to even on the 16 dropped bits; overflow carries into the
+    exponent (to Inf); NaN stays NaN (quiet bit set).  This is the rounding of
+    a GEMM output stored in bf16 (the fused-epilogue reading R19: the next
+    linear quantizes bf16(C))."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (b & 0x7FFFFFFF) > 0x7F800000
+    lsb = (b >> 16) & 1
+    r = ((b + 0x7FFF + lsb) >> 16) & 0xFFFF
+    r = np.where(nan, ((b >> 16) | 0x40) & 0xFFFF, r)
+    return r.astype(np.uint16)

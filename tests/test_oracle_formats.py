@@ -190,3 +190,46 @@ def test_bf16_decode():
     f = formats.bf16_to_f32(bits)
     assert f[0] == 1.0 and f[1] == -1.0 and f[2] == 0 and np.signbit(f[3])
     assert np.isinf(f[4]) and f[5] == np.float32(2.0 ** -133)
+
+
+def test_f32_to_bf16_rne_worked_cases():
+    """Hand-worked roundings of the 16 dropped bits: below, at and above the
+    halfway point, ties to the even pattern, the carry into the exponent and
+    into Inf, signs, subnormals and NaN."""
+    cases = {
+        0x3F800000: 0x3F80,  # 1.0
+        0x3F807FFF: 0x3F80,  # just below half an ulp: down
+        0x3F808000: 0x3F80,  # tie, 0x3F80 is even: down
+        0x3F808001: 0x3F81,  # just above: up
+        0x3F818000: 0x3F82,  # tie, 0x3F81 is odd: up to the even one
+        0x3FFF8000: 0x4000,  # tie at the top of the binade: the carry bumps the exponent
+        0xBFC00000: 0xBFC0,  # -1.5
+        0x7F7FFFFF: 0x7F80,  # largest fp32 rounds to +Inf
+        0xFF7F8000: 0xFF80,  # tie at the top, odd: -Inf
+        0x7F800000: 0x7F80,  # +Inf
+        0x00008000: 0x0000,  # subnormal tie to even (zero)
+        0x00018000: 0x0002,  # subnormal tie, odd: up
+        0x80000000: 0x8000,  # -0
+    }
+    x = np.array(list(cases), dtype=np.uint32).view(np.float32)
+    got = formats.f32_to_bf16_rne(x)
+    assert got.tolist() == list(cases.values())
+    nan = formats.f32_to_bf16_rne(np.array([0x7FC00000, 0x7F800001, 0xFFA00000], np.uint32).view(np.float32))
+    assert np.all((nan & 0x7F80) == 0x7F80) and np.all((nan & 0x7F) != 0)
+
+
+def test_f32_to_bf16_rne_against_torch_cast():
+    """A library routine: torch's CPU fp32 -> bfloat16 cast (round to nearest
+    even) on random finite patterns and on every tie pattern (low half 0x8000)
+    and its two neighbours."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    rand = rng.integers(0, 2**32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    ties = np.concatenate([hi | 0x7FFF, hi | 0x8000, hi | 0x8001])
+    bits = np.concatenate([rand, ties])
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(formats.f32_to_bf16_rne(x), want)
