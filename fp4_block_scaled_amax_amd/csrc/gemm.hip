@@ -614,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     if (QUANT) {
         float* rlut = reinterpret_cast<float*>(smem + kQTile);
         const Ctx ctx = make_ctx(*q.ts);
-        rlut[tid] = rcp_entry((uint32_t)tid, ctx.ts);
+        rlut[tid] = q.stochastic ? rcp_entry<true>((uint32_t)tid, ctx.ts) : rcp_entry<false>((uint32_t)tid, ctx.ts);
         __syncthreads();  // tile and table visible
         if (q.row_codes) {
             if (q.stochastic) quantize_tile_rows<true>(smem, ctx, rlut, q, m0, n0, M, N);

@@ -8,9 +8,10 @@
 // refined division of formats.hpp (equal to IEEE division wherever the code
 // depends on it); the UE5M3 code from the bits of s_raw without branches
 // (normal, subnormal, saturated); r = 1 / (ts * s_b) from a 256-entry table
-// each workgroup builds with IEEE division; round-to-nearest payloads from
-// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 (equal to the nearest-even
-// definition for every non-NaN fp32 input, checked on gfx950); blocks the
+// each workgroup builds with IEEE division (times 2^17 for stochastic
+// rounding); round-to-nearest payloads from v_cvt_scalef32_pk_fp4_f32 with
+// scale 1.0 (equal to the nearest-even definition for every non-NaN fp32
+// input, checked on gfx950), stochastic ones from its SR sibling; blocks the
 // fast path cannot take are redone by the definition.
 #pragma once
 
@@ -63,12 +64,18 @@ __device__ __noinline__ BlockScale block_scale_general(uint32_t amax16, float ts
 
 // Reciprocal table entry for scale code c: RN(1 / RN(ts * s_c)) by IEEE
 // division, 0 for code 0; NaN marks codes the fast path must not use (the
-// NaN code, and reciprocals that overflow or are NaN).
+// NaN code, and reciprocals that overflow or are NaN).  With stochastic
+// rounding the entry is that reciprocal times 2^17 (an exact scaling, see
+// encode8), and also NaN where the scaled value would overflow or where the
+// reciprocal is at most 2^-17 (there an element could round to 0 in
+// x * r but not in x * r * 2^17).
+template <bool SR>
 __device__ __forceinline__ float rcp_entry(uint32_t c, float ts) {
     if (c == 0u) return 0.0f;
     if (c == kUe5m3Nan) return __uint_as_float(0x7FC00000u);
     const float r = 1.0f / (ts * ue5m3_decode(c));
-    return fabsf(r) <= 3.4028235e38f ? r : __uint_as_float(0x7FC00000u);
+    if (!SR) return fabsf(r) <= 3.4028235e38f ? r : __uint_as_float(0x7FC00000u);
+    return (r > 0x1p-17f && r <= 0x1p110f) ? r * 0x1p17f : __uint_as_float(0x7FC00000u);
 }
 
 // Fast block scale.  s = amax / K by the refined division (exact for
@@ -99,9 +106,10 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t amax16, const Ctx& c,
 }
 
 // 8 fp32 values -> 8 E2M1 nibbles (element k in nibble k).
-// RNE: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1
-// exactly as the nearest-even definition does, sign included (checked on
-// gfx950 for all 2^32 non-NaN inputs).  SR: magnitude index from formats.hpp.
+// RNE: v holds x * r.  v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an
+// fp32 value to E2M1 exactly as the nearest-even definition does, sign
+// included (checked on gfx950 for all 2^32 non-NaN inputs).
+// SR: v holds x * r * 2^17 (the table entries carry the 2^17).
 template <bool SR>
 __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rnd) {
     if (!SR) {
@@ -112,41 +120,35 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
         p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
         return p;
     }
-    // Stochastic rounding on v_cvt_scalef32_sr_pk_fp4_f32.  Measured on
-    // gfx950: its first element rounds up iff floor(f * 2^32) + seed >= 2^32,
-    // f being the fraction of |v| between its two E2M1 neighbours (sign
-    // copied, saturation at 6); its second element sees seed << 1, so each
-    // element gets an instruction of its own (the other slot holds +0, which
-    // encodes to 0 whatever the seed).  With seed = ~(u << 16) =
-    // (65535 - u) * 2^16 + 65535 that is "round up iff f * 2^32 > u * 2^16",
-    // i.e. u < 65536 f, the definition -- exactly wherever f * 2^32 is an
-    // integer, which holds for |v| >= 2^-10.  Elements below 2^-10 (rare:
-    // far below their block's largest) are redone by the definition.  Only
-    // byte 0 of the instruction's result is defined here.
+    // Stochastic rounding on v_cvt_scalef32_sr_pk_fp4_f32, which divides its
+    // input by the scale operand.  Measured on gfx950: its first element
+    // rounds up iff F + seed >= 2^32, F being the fraction f of |v| between
+    // its two E2M1 neighbours (sign copied, saturation at 6, +-Inf to +-6)
+    // taken to 22 bits: F = floor(f * 2^22) * 2^10; its second element sees
+    // seed << 1, so each element gets an instruction of its own (the other
+    // slot holds +0, which encodes to 0 whatever the seed).  The definition,
+    // round up iff u < 65536 f, depends on f only through ceil(65536 f), so
+    // |v| is first rounded up to a multiple of 2^-17: f becomes
+    // ceil(65536 f) / 65536 in [0, 2) (and keeps the same ceil(65536 f) in
+    // [2, 6) as well, where the grid step is 1 or 2), F is then exact, and
+    // with seed = ~(u << 16) = 2^32 - 1 - u * 2^16 the instruction rounds up
+    // iff ceil(65536 f) > u, i.e. iff u < 65536 f -- for every v, tiny ones
+    // included.  The rounding up is ceil(|x r 2^17|) with x's sign, and the
+    // scale operand 2^17 undoes the 2^17.  Only byte 0 of the result is
+    // defined here.
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     uint32_t p = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t w = rnd.v[j];  // u of element 2j in the low half, of 2j + 1 in the high half
-        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{v[2 * j], 0.0f}, ~(w << 16),
-                                                                         1.0f, 0);
-        const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
-            0u, f32x2_t{v[2 * j + 1], 0.0f}, ~(w & 0xFFFF0000u), 1.0f, 0);
+        const float a = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(v[2 * j]))) |
+                                        (__float_as_uint(v[2 * j]) & 0x80000000u));
+        const float b = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(v[2 * j + 1]))) |
+                                        (__float_as_uint(v[2 * j + 1]) & 0x80000000u));
+        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{a, 0.0f}, ~(w << 16), 0x1p17f, 0);
+        const uint32_t hi =
+            __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{b, 0.0f}, ~(w & 0xFFFF0000u), 0x1p17f, 0);
         p |= ((lo & 0xFu) | ((hi & 0xFu) << 4)) << (8 * j);
-    }
-    // one test per 8 elements (v is finite here): the smallest magnitude
-    const float mn = fminf(fminf(fminf(fabsf(v[0]), fabsf(v[1])), fminf(fabsf(v[2]), fabsf(v[3]))),
-                           fminf(fminf(fabsf(v[4]), fabsf(v[5])), fminf(fabsf(v[6]), fabsf(v[7]))));
-    if (__builtin_expect(mn < 0x1p-10f, 0)) {
-        // |v| < 2^-10 < 0.5: the neighbours are 0 and 0.5 and 65536 f = |v| * 2^17
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (fabsf(v[k]) < 0x1p-10f) {
-                const uint32_t up = (float)sr_u16(rnd, k) < fabsf(v[k]) * 0x1p17f ? 1u : 0u;
-                const uint32_t sign = (__float_as_uint(v[k]) >> 28) & 8u;
-                p = (p & ~(0xFu << (4 * k))) | ((sign | up) << (4 * k));
-            }
-        }
     }
     return p;
 }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         ctx.yK = 1.0f / ctx.K;
         ctx.fastK = ctx.K >= 0x1p-100f && ctx.K <= 0x1p100f;
         ctx.tinyOK = ctx.K >= 1.0f;
-        rlut[t] = rcp_entry((uint32_t)t, ctx.ts);
+        rlut[t] = rcp_entry<SR>((uint32_t)t, ctx.ts);
     }
 
     // ---- row half-block amax (bf16 magnitude bits; NaN sorts above Inf)
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
     ctx.yK = 1.0f / ctx.K;
     ctx.fastK = ctx.K >= 0x1p-100f && ctx.K <= 0x1p100f;
     ctx.tinyOK = ctx.K >= 1.0f;
-    rlut[t] = rcp_entry((uint32_t)t, ctx.ts);
+    rlut[t] = rcp_entry<SR>((uint32_t)t, ctx.ts);
 
     // ---- tile amax (bf16 magnitude bits; NaN sorts above Inf)
     uint32_t m2 = 0u;
