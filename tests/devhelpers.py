@@ -59,14 +59,24 @@ def assert_quant_equal(q_dev, bits, ts, rounding, seed, offset, orientation, row
 def assert_gemm_close(c_gpu, a_codes, a_scales, ts_a, b_codes, b_scales, ts_b, rows=None, cols=None,
                       rtol=1e-5):
     """|C_gpu - C_ref| <= rtol * |tsA tsB| * sum|a||b| per element, on all
-    elements or on the sampled (rows[t], cols[t]) entries.  NaN must match."""
+    elements or on the sampled (rows[t], cols[t]) entries.  NaN must match.
+    The operands are the oracle's (never codes the GPU produced)."""
     if rows is None:
         ref, bound = gemm.gemm_nt(a_codes, a_scales, ts_a, b_codes, b_scales, ts_b)
         got = c_gpu.astype(np.float64)
-    else:
-        ref, bound = gemm.gemm_nt_entries(a_codes, a_scales, ts_a, b_codes, b_scales, ts_b,
-                                          rows, cols)
-        got = c_gpu[rows, cols].astype(np.float64)
+        return _close(got, ref, bound, rtol)
+    return assert_entries_close(c_gpu[rows, cols], a_codes, a_scales, ts_a, b_codes, b_scales, ts_b,
+                                rows, cols, rtol)
+
+
+def assert_entries_close(got, a_codes, a_scales, ts_a, b_codes, b_scales, ts_b, ia, ib, rtol=1e-5):
+    """GPU entries got[t] against entry (ia[t], ib[t]) of the oracle's
+    tsA tsB A B^T, where A and B hold only the operand rows the entries use."""
+    ref, bound = gemm.gemm_nt_entries(a_codes, a_scales, ts_a, b_codes, b_scales, ts_b, ia, ib)
+    return _close(np.asarray(got).astype(np.float64), ref, bound, rtol)
+
+
+def _close(got, ref, bound, rtol):
     nan_ref = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan_ref), "NaN pattern differs"
     err = np.abs(got - ref)[~nan_ref]
@@ -75,6 +85,21 @@ def assert_gemm_close(c_gpu, a_codes, a_scales, ts_a, b_codes, b_scales, ts_b, r
     assert np.all(err <= lim), (f"gemm error {err.flat[worst]:.3e} > {lim.flat[worst]:.3e} "
                                 f"(ref {ref[~nan_ref].flat[worst]:.6e})")
     return float(np.max(err / np.maximum(bound[~nan_ref], 1e-300))) if err.size else 0.0
+
+
+def oracle_operand(bits, ts, rounding, seed, offset, orientation, q_gpu=None, rows=None):
+    """The oracle's quantization of bf16 `bits` in one orientation (output
+    rows `rows` only, with their true coordinates, when given).  With q_gpu,
+    the GPU's codes and scales on those rows must equal it bit for bit.
+    Returns (codes, scales)."""
+    codes, scales = quantize.quantize_blockscale(bits, ts, rounding, seed, offset, orientation, rows=rows)
+    if q_gpu is not None:
+        gc, gs = host(q_gpu.codes), host(q_gpu.scales)
+        if rows is not None:
+            gc, gs = gc[rows], gs[rows]
+        assert np.array_equal(gs, scales), f"scales differ (orientation {orientation})"
+        assert np.array_equal(gc, codes), f"codes differ (orientation {orientation})"
+    return codes, scales
 
 
 def sample_rows(n, k, seed):

@@ -1,8 +1,10 @@
 """Maximum-size edge cases: tensors past 2^31 elements and GEMM outputs past
-2^31 entries, so every byte offset needs 64 bits.  Inputs are generated on
-the device from a seeded generator; sampled rows / entries are compared with
-the oracle (round to nearest: the codes do not depend on coordinates, so a
-sampled row can be quantized on its own).
+2^31 entries, so every byte offset needs 64 bits.  The input is a seeded
+block from the input generator (4093 x 16384: a row period that is not a
+power of two, so an offset that wrapped would read different data) tiled on
+the device to 133120 rows; sampled rows / entries are compared with the
+oracle on the generator's block (round to nearest: the codes do not depend
+on coordinates, so a sampled row can be quantized on its own).
 
 Sizes: x is 133120 x 16384 bf16 (2.18e9 elements, 4.4 GB; outputs 1.2 GB per
 orientation); C is 65536 x 36864 fp32 (2.4e9 entries, 9.7 GB)."""
@@ -12,13 +14,15 @@ import pytest
 
 import fp4_block_scaled_amax_amd as lib
 from oracle import quantize, quantize2d
+from workloads import random_bf16
 
-from devhelpers import dev_scalar, host
+from devhelpers import dev_bf16, dev_scalar, host
 
 pytestmark = pytest.mark.gpu
 
 R, C = 133120, 16384
-ROWS = [0, 1, 8191, 65535, 65536, 131071, R - 16, R - 1]
+PERIOD = 4093
+ROWS = np.array([0, 1, 8191, 65535, 65536, 131071, 131072, R - 16, R - 1])
 COLS = [0, 7, 4096, C - 1]
 
 
@@ -26,36 +30,33 @@ COLS = [0, 7, 4096, C - 1]
 def big_x(cuda_device):
     import torch
 
-    g = torch.Generator(device="cuda").manual_seed(20260)
-    x = torch.randn((R, C), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    block = random_bf16((PERIOD, C), seed=20260)
+    blk = dev_bf16(block)
+    x = blk.repeat(-(-R // PERIOD), 1)[:R].contiguous()
+    del blk
     assert x.numel() > 2**31
-    yield x
+    yield block, x
     del x
     torch.cuda.empty_cache()
-
-
-def _bits(t):
-    import torch
-
-    return host(t.contiguous().view(torch.int16)).view(np.uint16)
 
 
 def test_quantize_past_2_31_elements(big_x):
     import torch
 
-    ts_val = np.float32(float(big_x.abs().max().float()) / 43008.0)
+    block, x = big_x
+    amax_ref = quantize.tensor_amax(block)
+    ts_val = np.float32(np.float32(amax_ref) / np.float32(43008.0))
     ts = dev_scalar(ts_val)
     amax = dev_scalar(0.0)
     qr = lib.empty_quantized(R, C, ts)
     qc = lib.empty_quantized(C, R, ts)
-    lib.quantize_blockscale(big_x, ts, lib.RNE, row=qr, col=qc, amax=amax)
+    lib.quantize_blockscale(x, ts, lib.RNE, row=qr, col=qc, amax=amax)
     torch.cuda.synchronize()
-    assert host(amax)[0] == np.float32(big_x.abs().max().float().item())
-    xr = _bits(big_x[ROWS])
-    c, s = quantize.quantize_blockscale(xr, ts_val, quantize.RNE)
-    assert np.array_equal(host(qr.codes[ROWS]), c) and np.array_equal(host(qr.scales[ROWS]), s)
-    xc = _bits(big_x[:, COLS])  # R x k: output rows of the transposed orientation
-    c, s = quantize.quantize_blockscale(xc, ts_val, quantize.RNE, orientation=1)
+    assert host(amax)[0] == amax_ref
+    c, s = quantize.quantize_blockscale(block[ROWS % PERIOD], ts_val, quantize.RNE)
+    assert np.array_equal(host(qr.codes[ROWS.tolist()]), c) and np.array_equal(host(qr.scales[ROWS.tolist()]), s)
+    cols = np.tile(block[:, COLS], (-(-R // PERIOD), 1))[:R]  # R x k: output rows of the transposed orientation
+    c, s = quantize.quantize_blockscale(cols, ts_val, quantize.RNE, orientation=1)
     assert np.array_equal(host(qc.codes[COLS]), c) and np.array_equal(host(qc.scales[COLS]), s)
     del qr, qc
 
@@ -63,14 +64,15 @@ def test_quantize_past_2_31_elements(big_x):
 def test_quantize_2d_past_2_31_elements(big_x):
     import torch
 
-    ts_val = np.float32(float(big_x.abs().max().float()) / 43008.0)
+    block, x = big_x
+    ts_val = np.float32(np.float32(quantize.tensor_amax(block)) / np.float32(43008.0))
     ts = dev_scalar(ts_val)
     qr = lib.empty_quantized(R, C, ts)
     qc = lib.empty_quantized(C, R, ts)
-    lib.quantize_blockscale_2d(big_x, ts, lib.RNE, row=qr, col=qc)
+    lib.quantize_blockscale_2d(x, ts, lib.RNE, row=qr, col=qc)
     torch.cuda.synchronize()
-    for g in (0, 4096, R // 16 - 1):  # 16-row groups
-        xs = _bits(big_x[16 * g:16 * g + 16])
+    for g in (0, 4096, 8192, R // 16 - 1):  # 16-row groups (8192: rows 131072.., past 2^31 elements)
+        xs = block[(16 * g + np.arange(16)) % PERIOD]
         rc, rs, cc, cs, _ = quantize2d.quantize_blockscale_2d(xs, ts_val, quantize.RNE)
         assert np.array_equal(host(qr.codes[16 * g:16 * g + 16]), rc)
         assert np.array_equal(host(qr.scales[16 * g:16 * g + 16]), rs)
