@@ -336,3 +336,25 @@ def test_config3_gradient_sr_whole_tensor(cuda_device):
     qr, qc = gpu_quantize(dev_bf16(dY), ts, lib.SR, seed=sr_seed(3), offset=0)
     assert_quant_equal(qr, dY, ts, lib.SR, sr_seed(3), 0, 0)
     assert_quant_equal(qc, dY, ts, lib.SR, sr_seed(3), 0, 1)
+
+
+def test_r4_operation_order_blocks(cuda_device):
+    """The worked blocks that separate reading R4's order of roundings from
+    its alternatives (tests/test_oracle_r4_order.py: tensor scales that are
+    not powers of two, values within one fp32 ulp of a UE5M3 or E2M1
+    midpoint), placed in row 0 and column 0 of a 16 x 16 tile so both output
+    orientations see them: the kernels' codes and scales equal the oracle's,
+    with round to nearest and with stochastic rounding."""
+    from test_oracle_r4_order import ELEMENT_CASES, SCALE_CASES
+
+    cases = [(a, t, 0) for a, t in SCALE_CASES] + [(a, t, x) for x, t, a in ELEMENT_CASES]
+    for amax_b, ts_b, x_b in cases:
+        tile = np.zeros((16, 16), dtype=np.uint16)
+        tile[0, 0] = amax_b
+        tile[0, 5] = tile[5, 0] = x_b
+        tile[0, 9] = tile[9, 0] = 0x8000 | x_b  # and its negative
+        ts = np.uint32(ts_b).view(np.float32)
+        for rounding in (lib.RNE, lib.SR):
+            qr, qc = gpu_quantize(dev_bf16(tile), ts, rounding, seed=5, offset=1)
+            assert_quant_equal(qr, tile, ts, rounding, 5, 1, 0)
+            assert_quant_equal(qc, tile, ts, rounding, 5, 1, 1)
