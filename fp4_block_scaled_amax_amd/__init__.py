@@ -99,15 +99,60 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _require(t, dtypes, name, dims=None):
+def _require(t, dtypes, name, dims=None, contiguous=False):
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
+    if not getattr(t, "is_cuda", False):
         raise ValueError(f"{name} must be a device (cuda) tensor")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dimensions")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _require_scalar(t, name):
+    """A device fp32 scalar (tensor scale, amax): one element."""
+    import torch
+
+    _require(t, (torch.float32,), name)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold exactly one fp32 value (has {t.numel()})")
+
+
+def _check_pair(codes, scales, rows, cols, name):
+    """Code and scale buffers of a rows x cols operand blocked along cols:
+    contiguous uint8 [rows][cols/2] and [rows][cols/16] on the device."""
+    import torch
+
+    _require(codes, (torch.uint8,), f"{name} codes", 2, contiguous=True)
+    _require(scales, (torch.uint8,), f"{name} scales", 2, contiguous=True)
+    if tuple(codes.shape) != (rows, cols // 2) or tuple(scales.shape) != (rows, cols // 16):
+        raise ValueError(f"{name}: codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not "
+                         f"match a {rows} x {cols} operand ([{rows}][{cols // 2}], [{rows}][{cols // 16}])")
+    if codes.device != scales.device:
+        raise ValueError(f"{name}: codes and scales are on different devices")
+
+
+def _check_operand(q, name):
+    """A Quantized operand: contiguous device codes [R][C/2] and scales
+    [R][C/16] (C % 16 == 0), and a one-element device fp32 tensor scale."""
+    if not isinstance(q, Quantized):
+        raise ValueError(f"{name} must be a Quantized operand")
+    _require(q.codes, (__import__("torch").uint8,), f"{name} codes", 2)
+    if q.codes.shape[1] % 8 != 0:
+        raise ValueError(f"{name}: cols ({q.codes.shape[1] * 2}) must be a multiple of 16")
+    _check_pair(q.codes, q.scales, q.codes.shape[0], q.codes.shape[1] * 2, name)
+    _require_scalar(q.ts, f"{name} ts")
+    if q.ts.device != q.codes.device:
+        raise ValueError(f"{name}: ts is on another device than its codes")
+
+
+def _same_device(name, *ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{name}: tensors on different devices {sorted(map(str, devs))}")
 
 
 @dataclass
@@ -144,24 +189,28 @@ def _quantize_operands(x, tensor_scale, row, col, amax):
     _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2)
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along its columns")
+    rows, cols = x.shape
+    rc, rs, cc, cs = _output_pairs(row, col, rows, cols)
+    if tensor_scale is not None:
+        _require_scalar(tensor_scale, "tensor_scale")
+    if amax is not None:
+        _require_scalar(amax, "amax")
+    _same_device("quantize", x, rc, rs, cc, cs, tensor_scale, amax)
+    return rows, cols, rc, rs, cc, cs
+
+
+def _output_pairs(row, col, rows, cols):
+    """(codes, scales) of the row-wise output (rows x cols, blocked along
+    cols) and of the transposed output (cols x rows, blocked along rows),
+    each None or checked: contiguous device uint8 of the exact shapes."""
     rc = rs = cc = cs = None
     if row is not None:
         rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
+        _check_pair(rc, rs, rows, cols, "row output")
     if col is not None:
         cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
-    for t, n in ((rc, "row codes"), (rs, "row scales"), (cc, "col codes"), (cs, "col scales")):
-        if t is not None:
-            _require(t, (torch.uint8,), n)
-    if tensor_scale is not None:
-        _require(tensor_scale, (torch.float32,), "tensor_scale")
-    if amax is not None:
-        _require(amax, (torch.float32,), "amax")
-    rows, cols = x.shape
-    if rc is not None and (tuple(rc.shape) != (rows, cols // 2) or tuple(rs.shape) != (rows, cols // 16)):
-        raise ValueError("row output buffers have the wrong shape")
-    if cc is not None and (tuple(cc.shape) != (cols, rows // 2) or tuple(cs.shape) != (cols, rows // 16)):
-        raise ValueError("col output buffers have the wrong shape")
-    return rows, cols, rc, rs, cc, cs
+        _check_pair(cc, cs, cols, rows, "col output")
+    return rc, rs, cc, cs
 
 
 def quantize_blockscale(x, tensor_scale, rounding=RNE, seed=0, offset=0, row=None, col=None,
@@ -193,27 +242,37 @@ def dequantize(q, out, stream=None):
     """out (fp32 [R][C]) = ts * s_b * e2m1 of the quantized operand q."""
     import torch
 
-    _require(out, (torch.float32,), "out", 2)
+    _check_operand(q, "q")
+    _require(out, (torch.float32,), "out", 2, contiguous=True)
     if tuple(out.shape) != (q.rows, q.cols):
         raise ValueError("out has the wrong shape")
+    _same_device("dequantize", q.codes, out)
     st = load_library().ue5m3fp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.ts), q.rows,
                                             q.cols, _ptr(out), _stream(stream))
     _check(st, "ue5m3fp4_dequantize")
     return out
 
 
-def _gemm_out(out, m, n):
+def _gemm_out(out, m, n, dtypes=None):
     import torch
 
-    _require(out, (torch.float32,), "out", 2)
+    _require(out, dtypes or (torch.float32,), "out", 2)
     if tuple(out.shape) != (m, n) or not out.is_contiguous():
-        raise ValueError(f"output must be a contiguous fp32 [{m}][{n}] tensor")
+        raise ValueError(f"output must be a contiguous [{m}][{n}] tensor")
+
+
+def _gemm_operands(a, b, out, na="A", nb="B"):
+    """Both operands checked, blocked along the same K, on out's device."""
+    _check_operand(a, na)
+    _check_operand(b, nb)
+    if a.cols != b.cols:
+        raise ValueError(f"{na} and {nb} disagree on the contraction axis ({a.cols} vs {b.cols})")
+    _same_device("gemm", a.codes, b.codes, out)
 
 
 def gemm_nt(a, b, out, stream=None):
     """out[M][N] = tsA * tsB * A B^T with A (M x K) and B (N x K) blocked along K."""
-    if a.cols != b.cols:
-        raise ValueError("A and B disagree on K")
+    _gemm_operands(a, b, out)
     _gemm_out(out, a.rows, b.rows)
     st = load_library().ue5m3fp4_gemm_nt(_ptr(a.codes), _ptr(a.scales), _ptr(a.ts),
                                          _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
@@ -227,13 +286,11 @@ def gemm_nt_bf16(a, b, out, amax=None, stream=None):
     amax (device fp32 scalar or None) receives max(amax, max|out|)."""
     import torch
 
-    if a.cols != b.cols:
-        raise ValueError("A and B disagree on K")
-    _require(out, (torch.bfloat16, torch.int16, torch.uint16), "out", 2)
-    if tuple(out.shape) != (a.rows, b.rows) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous ({a.rows}, {b.rows}) tensor")
+    _gemm_operands(a, b, out)
+    _gemm_out(out, a.rows, b.rows, (torch.bfloat16, torch.int16, torch.uint16))
     if amax is not None:
-        _require(amax, (torch.float32,), "amax")
+        _require_scalar(amax, "amax")
+        _same_device("gemm_nt_bf16", out, amax)
     st = load_library().ue5m3fp4_gemm_nt_bf16(_ptr(a.codes), _ptr(a.scales), _ptr(a.ts),
                                               _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), a.rows,
                                               b.rows, a.cols, _ptr(out), _ptr(amax), _stream(stream))
@@ -249,27 +306,14 @@ def gemm_nt_bf16_quantized(a, b, out, out_ts, rounding=RNE, seed=0, offset=0, ro
     write.  out_ts: the output's device fp32 tensor scale."""
     import torch
 
-    if a.cols != b.cols:
-        raise ValueError("A and B disagree on K")
+    _gemm_operands(a, b, out)
     M, N = a.rows, b.rows
-    _require(out, (torch.bfloat16, torch.int16, torch.uint16), "out", 2)
-    if tuple(out.shape) != (M, N) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous ({M}, {N}) tensor")
-    _require(out_ts, (torch.float32,), "out_ts")
+    _gemm_out(out, M, N, (torch.bfloat16, torch.int16, torch.uint16))
+    _require_scalar(out_ts, "out_ts")
     if amax is not None:
-        _require(amax, (torch.float32,), "amax")
-    rc = rs = cc = cs = None
-    if row is not None:
-        rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
-        if tuple(rc.shape) != (M, N // 2) or tuple(rs.shape) != (M, N // 16):
-            raise ValueError("row output buffers have the wrong shape")
-    if col is not None:
-        cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
-        if tuple(cc.shape) != (N, M // 2) or tuple(cs.shape) != (N, M // 16):
-            raise ValueError("col output buffers have the wrong shape")
-    for t, n in ((rc, "row codes"), (rs, "row scales"), (cc, "col codes"), (cs, "col scales")):
-        if t is not None:
-            _require(t, (torch.uint8,), n)
+        _require_scalar(amax, "amax")
+    rc, rs, cc, cs = _output_pairs(row, col, M, N)
+    _same_device("gemm_nt_bf16_quantized", out, out_ts, amax, rc, rs, cc, cs)
     st = load_library().ue5m3fp4_gemm_nt_bf16_quantized(
         _ptr(a.codes), _ptr(a.scales), _ptr(a.ts), _ptr(b.codes), _ptr(b.scales), _ptr(b.ts), M, N,
         a.cols, _ptr(out), _ptr(amax), _ptr(out_ts), int(rounding), int(seed), int(offset), _ptr(rc),
@@ -284,12 +328,15 @@ def gemm_nt_mxfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out, stream=
     import torch
 
     for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
-        _require(t, (torch.uint8,), n, 2)
+        _require(t, (torch.uint8,), n, 2, contiguous=True)
+    _require_scalar(a_ts, "a_ts")
+    _require_scalar(b_ts, "b_ts")
     m, k = a_codes.shape[0], a_codes.shape[1] * 2
     n = b_codes.shape[0]
     if b_codes.shape[1] * 2 != k or tuple(a_scales.shape) != (m, k // 32) or tuple(b_scales.shape) != (n, k // 32):
         raise ValueError("MXFP4 operand shapes disagree")
     _gemm_out(out, m, n)
+    _same_device("gemm_nt_mxfp4", a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out)
     st = load_library().ue5m3fp4_gemm_nt_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(a_ts), _ptr(b_codes),
                                                _ptr(b_scales), _ptr(b_ts), m, n, k, _ptr(out),
                                                _stream(stream))
@@ -299,6 +346,8 @@ def gemm_nt_mxfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out, stream=
 
 def gemm_fprop(x_row, w_row, y, stream=None):
     """Y [tokens][out] = X W^T from X and W quantized row-wise."""
+    _check_operand(x_row, "x_row")
+    _check_operand(w_row, "w_row")
     tokens, in_f = x_row.rows, x_row.cols
     out_f = w_row.rows
     if w_row.cols != in_f:
@@ -313,6 +362,8 @@ def gemm_fprop(x_row, w_row, y, stream=None):
 
 def gemm_dgrad(dy_row, w_col, dx, stream=None):
     """dX [tokens][in] = dY W from dY row-wise and W's transposed output."""
+    _check_operand(dy_row, "dy_row")
+    _check_operand(w_col, "w_col")
     tokens, out_f = dy_row.rows, dy_row.cols
     in_f = w_col.rows
     if w_col.cols != out_f:
@@ -328,6 +379,8 @@ def gemm_dgrad(dy_row, w_col, dx, stream=None):
 
 def gemm_wgrad(dy_col, x_col, dw, stream=None):
     """dW [out][in] = dY^T X from the transposed outputs of dY and X."""
+    _check_operand(dy_col, "dy_col")
+    _check_operand(x_col, "x_col")
     out_f, tokens = dy_col.rows, dy_col.cols
     in_f = x_col.rows
     if x_col.cols != tokens:
@@ -352,18 +405,11 @@ def quantize_current_scaling(x, tensor_scale, amax, rounding=RNE, seed=0, offset
     _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2)
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along its columns")
-    _require(tensor_scale, (torch.float32,), "tensor_scale")
-    _require(amax, (torch.float32,), "amax")
-    rc = rs = cc = cs = None
-    if row is not None:
-        rc, rs = (row.codes, row.scales) if isinstance(row, Quantized) else row
-    if col is not None:
-        cc, cs = (col.codes, col.scales) if isinstance(col, Quantized) else col
+    _require_scalar(tensor_scale, "tensor_scale")
+    _require_scalar(amax, "amax")
     rows, cols = x.shape
-    if rc is not None and (tuple(rc.shape) != (rows, cols // 2) or tuple(rs.shape) != (rows, cols // 16)):
-        raise ValueError("row output buffers have the wrong shape")
-    if cc is not None and (tuple(cc.shape) != (cols, rows // 2) or tuple(cs.shape) != (cols, rows // 16)):
-        raise ValueError("col output buffers have the wrong shape")
+    rc, rs, cc, cs = _output_pairs(row, col, rows, cols)
+    _same_device("quantize_current_scaling", x, tensor_scale, amax, rc, rs, cc, cs)
     st = load_library().ue5m3fp4_quantize_current_scaling(
         _ptr(x), rows, cols, x.stride(0), float(max_safe), int(rounding), int(seed), int(offset),
         _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs), _ptr(tensor_scale), _ptr(amax), _stream(stream))
@@ -374,10 +420,9 @@ def update_tensor_scale(amax_running, tensor_scale, step, period=1,
                         max_safe=MAX_SAFE_DEFAULT, stream=None):
     """Periodic refresh: at step % period == 0, ts = amax / (6 max_safe) if
     amax is finite and > 0, and amax is reset to 0 (both device scalars)."""
-    import torch
-
-    _require(amax_running, (torch.float32,), "amax_running")
-    _require(tensor_scale, (torch.float32,), "tensor_scale")
+    _require_scalar(amax_running, "amax_running")
+    _require_scalar(tensor_scale, "tensor_scale")
+    _same_device("update_tensor_scale", amax_running, tensor_scale)
     st = load_library().ue5m3fp4_update_tensor_scale(_ptr(amax_running), _ptr(tensor_scale),
                                                      int(step), int(period), float(max_safe),
                                                      _stream(stream))

@@ -153,9 +153,16 @@ UE5M3FP4_API int ue5m3fp4_quantize_current_scaling(const uint16_t* x, int64_t ro
                                       uint8_t* col_scales, float* tensor_scale, float* amax_out,
                                       void* stream);
 
-/* out[i][j] = fp32(fp32(e2m1 * ue5m3) * ts) for a quantized rows x cols
- * operand (the product q * s_b is exact, so there is one rounding).  Blocks
- * with scale 0xFF give NaN.  out is fp32 [rows][cols].  cols % 16 == 0. */
+/* Dequantize one block-scaled operand: the value that the UE5M3 paper's
+ * two-level format stores ("UE5M3 FP4 Block Scaling for Stable Language
+ * Model Pretraining", abstract: E2M1 payloads, one unsigned-E5M3 scale per
+ * 16-element block, an fp32 tensor scale):
+ *   out[i][j] = fp32(fp32(e2m1 * ue5m3) * ts) for a quantized rows x cols
+ * operand (the product q * s_b is exact, so there is one rounding).
+ *   codes [rows][cols/2], scales [rows][cols/16] (the quantizer's layouts),
+ *   tensor_scale: device fp32 scalar; out: fp32 [rows][cols], row stride cols.
+ * Blocks with scale 0xFF give NaN.  cols % 16 == 0 (UE5M3FP4_ESHAPE); NULL
+ * pointers UE5M3FP4_EINVAL; misaligned pointers UE5M3FP4_EALIGN. */
 UE5M3FP4_API int ue5m3fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                         int64_t rows, int64_t cols, float* out, void* stream);
 
@@ -228,7 +235,14 @@ UE5M3FP4_API int ue5m3fp4_gemm_fprop(const uint8_t* x_codes, const uint8_t* x_sc
                         int64_t tokens, int64_t in_features, int64_t out_features, float* y,
                         void* stream);
 
-/* dgrad: dX = dY W.
+/* dgrad: dX = dY W.  The second of the three training GEMMs of a linear
+ * layer ("Rethinking Shrinkage Bias in LLM FP4 Pretraining ... UFP4
+ * Recipe", abstract), run on block-scaled FP4 operands with stochastic
+ * rounding on dY only ("UE5M3 FP4 Block Scaling ...", abstract: selective
+ * stochastic rounding for backward gradients); W enters through its
+ * transposed quantization, blocked along the contraction axis ("Stable FP4
+ * Training via Transposition-Invariant Block Quantization", related-papers
+ * summary: 1-D blocks give W and W^T different scales).
  *   dy: dY [tokens][out] quantized row-wise (codes [tokens][out/2]);
  *   wt: the transposed output of W's quantization, W^T [in][out] blocked
  *       along out (codes [in][out/2]);
@@ -238,7 +252,11 @@ UE5M3FP4_API int ue5m3fp4_gemm_dgrad(const uint8_t* dy_codes, const uint8_t* dy_
                         int64_t tokens, int64_t in_features, int64_t out_features, float* dx,
                         void* stream);
 
-/* wgrad: dW = dY^T X.
+/* wgrad: dW = dY^T X.  The third training GEMM of a linear layer ("Rethinking
+ * Shrinkage Bias in LLM FP4 Pretraining ... UFP4 Recipe", abstract): it
+ * contracts over tokens, so both operands are the transposed quantizations
+ * of dY and X, each blocked along tokens ("Stable FP4 Training via
+ * Transposition-Invariant Block Quantization", related-papers summary).
  *   dyt: the transposed output of dY's quantization, dY^T [out][tokens]
  *        blocked along tokens (codes [out][tokens/2]);
  *   xt:  the transposed output of X's quantization, X^T [in][tokens]
