@@ -159,6 +159,14 @@ __device__ __forceinline__ U32x4 sr_words(uint64_t n, uint32_t offset, uint32_t 
                          (uint32_t)(seed >> 32));
 }
 
+// The same for a call number below 2^32 (the counter's second word is 0):
+// the first half of rounds 1 and 2 then depends only on the offset, the
+// orientation and the key, which are the same for every lane of a launch,
+// so that part is computed once per wave instead of per lane.
+__device__ __forceinline__ U32x4 sr_words32(uint32_t n, uint32_t offset, uint32_t o, uint64_t seed) {
+    return philox4x32_10(n, 0u, offset, o, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
 __device__ __forceinline__ uint32_t sr_u16(const U32x4& w, int k) {
     return (w.v[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
 }

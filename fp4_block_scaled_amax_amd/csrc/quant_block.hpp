@@ -105,6 +105,25 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t amax16, const Ctx& c,
     return b;
 }
 
+// Stochastic rounding of the element pair (a, b) into byte J of p (a in the
+// low nibble), with the random word w (u of a in its low half, of b in its
+// high half); a and b hold x * r * 2^17.  See encode8.
+template <int J>
+__device__ __forceinline__ void sr_pair(uint32_t& p, float a, float b, uint32_t w) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t nw = ~w;
+    const float ra = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(a))) | (__float_as_uint(a) & 0x80000000u));
+    const float rb = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(b))) | (__float_as_uint(b) & 0x80000000u));
+    // byte 0 of each result holds the element's code (low nibble) and the
+    // +0 slot's code 0 (high nibble); its other bytes are not defined
+    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{ra, 0.0f}, (nw << 16) | 0xFFFFu, 0x1p17f, 0);
+    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{rb, 0.0f}, nw | 0xFFFFu, 0x1p17f, 0);
+    const uint32_t pair = (hi << 4) | lo;  // byte 0: code of a | code of b << 4
+    // byte J of p <- byte 0 of pair (selector 4), the other bytes of p kept
+    constexpr uint32_t kSel = (J == 0 ? 0x03020104u : J == 1 ? 0x03020400u : J == 2 ? 0x03040100u : 0x04020100u);
+    p = __builtin_amdgcn_perm(pair, p, kSel);
+}
+
 // 8 fp32 values -> 8 E2M1 nibbles (element k in nibble k).
 // RNE: v holds x * r.  v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an
 // fp32 value to E2M1 exactly as the nearest-even definition does, sign
@@ -134,22 +153,18 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
     // with seed = ~(u << 16) = 2^32 - 1 - u * 2^16 the instruction rounds up
     // iff ceil(65536 f) > u, i.e. iff u < 65536 f -- for every v, tiny ones
     // included.  The rounding up is ceil(|x r 2^17|) with x's sign, and the
-    // scale operand 2^17 undoes the 2^17.  Only byte 0 of the result is
-    // defined here.
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    // scale operand 2^17 undoes the 2^17.  Only byte 0 of the instruction's
+    // result is defined here (the compiler does not carry the other bytes
+    // of its first operand through): a shift-or joins the two codes of a
+    // pair in one byte and a byte permute places it.  Seeds: ~(u << 16) is
+    // (~w << 16) | 0xFFFF for the low half of w, and ~w | 0xFFFF for the high
+    // half (the instruction reads only the high 16 bits of the seed plus the
+    // carry that the all-ones low bits give).
     uint32_t p = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t w = rnd.v[j];  // u of element 2j in the low half, of 2j + 1 in the high half
-        const float a = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(v[2 * j]))) |
-                                        (__float_as_uint(v[2 * j]) & 0x80000000u));
-        const float b = __uint_as_float(__float_as_uint(__builtin_ceilf(fabsf(v[2 * j + 1]))) |
-                                        (__float_as_uint(v[2 * j + 1]) & 0x80000000u));
-        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{a, 0.0f}, ~(w << 16), 0x1p17f, 0);
-        const uint32_t hi =
-            __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{b, 0.0f}, ~(w & 0xFFFF0000u), 0x1p17f, 0);
-        p |= ((lo & 0xFu) | ((hi & 0xFu) << 4)) << (8 * j);
-    }
+    sr_pair<0>(p, v[0], v[1], rnd.v[0]);
+    sr_pair<1>(p, v[2], v[3], rnd.v[1]);
+    sr_pair<2>(p, v[4], v[5], rnd.v[2]);
+    sr_pair<3>(p, v[6], v[7], rnd.v[3]);
     return p;
 }
 

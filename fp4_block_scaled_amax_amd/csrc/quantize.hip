@@ -184,7 +184,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const int64_t c0 = C0 + 8 * u;
     const bool col_ok = c0 < cols;
     u32x4 w[kRowsPerThread];
-    {
+    if (interior) {
+        // one base address, then a stride common to the launch
+        const uint16_t* src = x + (R0 + rbase) * ld + c0;
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k)
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(8 * k) * ld));
+    } else {
         const uint16_t* src = x + (col_ok ? c0 : cols - 8);
 #pragma unroll
         for (int k = 0; k < kRowsPerThread; ++k) {
@@ -194,12 +200,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
 
     // Random words of the row-wise output (stochastic rounding): they depend
-    // on coordinates only.  Row-only calls draw them here, while the loads are
-    // in flight; with the transposed output as well, the 32 registers they
-    // would hold meanwhile cost a resident workgroup, so they are drawn where
-    // they are used.
+    // on coordinates only -- call n of row R0 + rbase + 8k is n0 + k * cols.
+    // Row-only calls draw them here, while the loads are in flight; with the
+    // transposed output as well, the 32 registers they would hold meanwhile
+    // cost a resident workgroup, so they are drawn where they are used.
+    // When every call number of the launch is below 2^32 (fewer than 2^35
+    // elements), the counter's second word is 0 (sr_words32).
+    const bool n32 = (uint64_t)rows * (uint64_t)cols < ((uint64_t)1 << 35);
+    const uint64_t n0 = ((uint64_t)(R0 + rbase) * (uint64_t)cols + (uint64_t)c0) >> 3;
     auto row_words = [&](int k) {
-        return sr_words(((uint64_t)(R0 + rbase + 8 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+        const uint64_t n = n0 + (uint64_t)k * (uint64_t)cols;
+        return n32 ? sr_words32((uint32_t)n, offset, 0u, seed) : sr_words(n, offset, 0u, seed);
     };
     constexpr bool kEarlyWords = SR && ROW && !COL;
     U32x4 early[kEarlyWords ? kRowsPerThread : 1];
@@ -341,11 +352,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             U32x4 rnd[4];
             if (SR) {
                 const uint64_t na = ((uint64_t)ca * (uint64_t)rows + (uint64_t)r0) >> 3;
-                const uint64_t nb = ((uint64_t)(ca + 1) * (uint64_t)rows + (uint64_t)r0) >> 3;
-                rnd[0] = sr_words(na, offset, 1u, seed);
-                rnd[1] = sr_words(na + 1u, offset, 1u, seed);
-                rnd[2] = sr_words(nb, offset, 1u, seed);
-                rnd[3] = sr_words(nb + 1u, offset, 1u, seed);
+                const uint64_t nb = na + (uint64_t)(rows >> 3);
+                if (n32) {
+                    rnd[0] = sr_words32((uint32_t)na, offset, 1u, seed);
+                    rnd[1] = sr_words32((uint32_t)na + 1u, offset, 1u, seed);
+                    rnd[2] = sr_words32((uint32_t)nb, offset, 1u, seed);
+                    rnd[3] = sr_words32((uint32_t)nb + 1u, offset, 1u, seed);
+                } else {
+                    rnd[0] = sr_words(na, offset, 1u, seed);
+                    rnd[1] = sr_words(na + 1u, offset, 1u, seed);
+                    rnd[2] = sr_words(nb, offset, 1u, seed);
+                    rnd[3] = sr_words(nb + 1u, offset, 1u, seed);
+                }
             }
             uint32_t code_a = ba.code, code_b = bb.code;
             if (__builtin_expect(ok, 1)) {
@@ -493,7 +511,12 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
     const bool col_ok = c0 < cols;
     const int64_t rb = R0 + 16 * wv + h;  // row of k = 0; row k is rb + 2k
     u32x4 w[8];
-    {
+    if (interior) {
+        const uint16_t* src = x + rb * ld + c0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(2 * k) * ld));
+    } else {
         const uint16_t* src = x + (col_ok ? c0 : cols - 8);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -501,6 +524,14 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
             w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r * ld));
         }
     }
+    // stochastic rounding: call n of row rb + 2k is n0 + k * cols / 4; the
+    // counter's second word is 0 when every call number is below 2^32
+    const bool n32 = (uint64_t)rows * (uint64_t)cols < ((uint64_t)1 << 35);
+    const uint64_t n0 = ((uint64_t)rb * (uint64_t)cols + (uint64_t)c0) >> 3;
+    auto row_words = [&](int k) {
+        const uint64_t n = n0 + (uint64_t)k * (uint64_t)(cols >> 2);
+        return n32 ? sr_words32((uint32_t)n, offset, 0u, seed) : sr_words(n, offset, 0u, seed);
+    };
 
     Ctx ctx;
     ctx.ts = *tensor_scale;
@@ -534,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = v[e] * b.r;
             U32x4 rnd;
-            if (SR) rnd = sr_words(((uint64_t)(rb + 2 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+            if (SR) rnd = row_words(k);
             packed[k] = encode8<SR>(v, rnd);
         }
     } else {
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             U32x4 rnd;
-            if (SR) rnd = sr_words(((uint64_t)(rb + 2 * k) * (uint64_t)cols + (uint64_t)c0) >> 3, offset, 0u, seed);
+            if (SR) rnd = row_words(k);
             packed[k] = encode8_general<SR>(w[k], b.code, b.r, rnd);
         }
     }
