@@ -24,7 +24,13 @@ HBM-resident buffer sets (the quantizer's bandwidth roofline).
 for the next layer (bf16 Y and its amax) against the fp32 output.
 `native_mxfp4` times the native MXFP4 comparison GEMM at the step's GEMM
 shape: its ratio to the UE5M3 GEMM is the cost of emulating UE5M3 scales.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+`configs` reports the other workloads call by call: the tiny linear's
+latency next to the oracle's seconds (256 x 256), the attention-projection
+layer (8192 x 4096 x 4096) and the dynamic-range stress layer at 4096^3 with
+stale tensor scales -- each quantization in GB/s, each GEMM in TFLOP/s.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step
+(about 10-20 s of host work), with the threads it ran on, the host's CPU
+count and the affinity mask.
 
 `--copy-calibration` instead runs a plain 256 MiB device copy, whose
 FETCH_SIZE / WRITE_SIZE counter readings give the scale factors that turn
@@ -46,6 +52,8 @@ HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA, MI355X
 TOKENS, HIDDEN, FFN = 8192, 4096, 16384
 QUANT_BYTES_PER_ELEM = 2.0 + 2 * 0.5625  # bf16 in; codes + scales out, both orientations
+CPU_GEMM_ROWS = 1024  # output rows of the up projection's fprop in the oracle's timed sample
+CPU_QUANT_ROWS = 2048  # output rows per orientation of dY_up in the oracle's timed sample
 
 
 def parse():
@@ -61,6 +69,8 @@ def parse():
                    help="skip timing the step captured as one HIP graph")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the epilogue-fusion and native-MXFP4 comparisons")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-call figures of configs 1, 3 and 5")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -133,6 +143,10 @@ def main():
     lib.load_library()
     torch.cuda.set_device(0)
     data = config(4)
+    cpu_sample = None
+    if not args.no_cpu_baseline:  # the oracle's sample rows, kept before the device copies
+        cpu_sample = {k: data[k] for k in ("dY_up", "W_up")}
+        cpu_sample["X_rows"] = data["X"][:CPU_GEMM_ROWS].copy()
     seed = sr_seed(4)
     layers = []
     tid = 0
@@ -262,8 +276,12 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_quantize_only:
         result["quantize_activations"] = quantize_only(lib, torch)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(step_flops, step_elems)
+    if not args.no_configs:
+        result["configs"] = {"config1_tiny_linear": config1_latency(lib, torch),
+                             "config3_attention_projection": linear_layer_timing(lib, torch, 3),
+                             "config5_dynamic_range_stale_x8": linear_layer_timing(lib, torch, 5, stale=8.0)}
+    if cpu_sample is not None:
+        result["cpu_baseline"] = cpu_baseline(step_flops, step_elems, cpu_sample)
     print(json.dumps(result), flush=True)
 
 
@@ -417,6 +435,118 @@ def dynamic_range_stress(lib, torch):
     return res
 
 
+def _event_ms(torch, fn, reps, warm=2):
+    """Mean ms per call of fn() over `reps` back-to-back calls (HIP events on
+    the current stream, after `warm` untimed calls)."""
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def config1_latency(lib, torch):
+    """The tiny linear (X and W 256 x 256 ~N(0,1) from seed 0, tensor scales
+    refreshed from their own amax, round to nearest): one pass of the path --
+    amax pass and refresh per tensor, row-wise quantization of X and W,
+    fprop (7 launches) -- timed on the GPU with HIP events (latency-bound,
+    no roofline claim), and the oracle's seconds for the same pass on the
+    host."""
+    import numpy as np
+
+    from oracle import gemm, quantize, tensor_scale
+    from workloads import config
+
+    d = config(1)
+    xs = {k: torch.from_numpy(v.view("int16")).cuda() for k, v in d.items()}
+    ts = {k: torch.ones(1, dtype=torch.float32, device="cuda") for k in d}
+    am = {k: torch.zeros(1, dtype=torch.float32, device="cuda") for k in d}
+    q = {k: lib.empty_quantized(256, 256, ts[k]) for k in d}
+    y = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+
+    def one_pass(_):
+        for k in ("X", "W"):
+            lib.quantize_blockscale(xs[k], None, amax=am[k])
+            lib.update_tensor_scale(am[k], ts[k], 0, 1)
+            lib.quantize_blockscale(xs[k], ts[k], lib.RNE, row=q[k])
+        lib.gemm_fprop(q["X"], q["W"], y)
+
+    ms = _event_ms(torch, one_pass, 50, warm=5)
+    t0 = time.perf_counter()
+    ops = {}
+    for k in ("X", "W"):
+        _, tsk = tensor_scale.update_tensor_scale(quantize.tensor_amax(d[k]), np.float32(1.0), 0, 1)
+        ops[k] = quantize.quantize_blockscale(d[k], tsk, quantize.RNE) + (tsk,)
+    gemm.gemm_nt(*ops["X"], *ops["W"])
+    oracle_s = time.perf_counter() - t0
+    return {"workload": "X, W 256x256 ~N(0,1) seed 0: amax + refresh + RNE row-wise quantize of X and W, "
+                        "fprop 256x256x256",
+            "gpu_us_per_pass": round(ms * 1e3, 2), "launches_per_pass": 7,
+            "oracle_s_per_pass": round(oracle_s, 4), "bound": "latency"}
+
+
+def linear_layer_timing(lib, torch, n, stale=None, reps=10, sets=4):
+    """One linear layer's hot path on config n's tensors (X, W, dY), call by
+    call: the quantization of each tensor (both orientations, amax on; RNE
+    for X and W, stochastic rounding for dY) in algorithmic GB/s, and fprop /
+    dgrad / wgrad in TFLOP/s.  Tensor scales come from a step-0 refresh of
+    each tensor's own amax, multiplied by `stale` when given (a scale from a
+    prior step's amax that is off by that factor).  Quantizer inputs and
+    outputs rotate over `sets` HBM-resident copies, so each call reads and
+    writes HBM rather than the 256 MB cache."""
+    from workloads import config, sr_seed
+
+    d = config(n)
+    T = {}
+    for tid, (name, rnd) in enumerate((("X", lib.RNE), ("W", lib.RNE), ("dY", lib.SR))):
+        t = Tensor(lib, torch, d[name], rnd, tid)
+        lib.quantize_blockscale(t.x, None, amax=t.amax)
+        if stale:
+            t.amax.mul_(stale)
+        lib.update_tensor_scale(t.amax, t.ts, 0, 1)
+        T[name] = t
+    del d
+    X, W, D = T["X"], T["W"], T["dY"]
+    tokens, in_f = X.row.rows, X.row.cols
+    out_f = W.row.rows
+    res = {"workload": f"config {n}: tokens {tokens}, in {in_f}, out {out_f}"
+                       + (f", tensor scales from an amax off by x{stale:g}" if stale else ""),
+           "quantize_peak_GBps": HBM_PEAK_GBS, "gemm_peak_TFLOPs": FP16_MFMA_PEAK_TFLOPS}
+    for name, t in T.items():
+        copies = [(t.x.clone(), lib.empty_quantized(t.row.rows, t.row.cols, t.ts),
+                   lib.empty_quantized(t.col.rows, t.col.cols, t.ts)) for _ in range(sets)]
+
+        def quant(i, t=t, copies=copies):
+            x, qr, qc = copies[i % len(copies)]
+            lib.quantize_blockscale(x, t.ts, t.rounding, sr_seed(n), i, row=qr, col=qc, amax=t.amax)
+
+        ms = _event_ms(torch, quant, reps * sets)
+        gbs = t.elems * QUANT_BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+        res[f"quantize_{name}"] = {"rounding": "sr" if t.rounding == lib.SR else "rne",
+                                   "us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del copies
+    Y = torch.empty((tokens, out_f), dtype=torch.float32, device="cuda")
+    dX = torch.empty((tokens, in_f), dtype=torch.float32, device="cuda")
+    dW = torch.empty((out_f, in_f), dtype=torch.float32, device="cuda")
+    for name, fn, a, b, c in (("fprop", lib.gemm_fprop, X.row, W.row, Y),
+                              ("dgrad", lib.gemm_dgrad, D.row, W.col, dX),
+                              ("wgrad", lib.gemm_wgrad, D.col, X.col, dW)):
+        flop = 2.0 * c.shape[0] * c.shape[1] * a.cols
+        ms = _event_ms(torch, lambda i, fn=fn, a=a, b=b, c=c: fn(a, b, c), reps)
+        tf = flop / (ms * 1e-3) / 1e12
+        res[name] = {"shape_MxNxK": f"{c.shape[0]}x{c.shape[1]}x{a.cols}", "us": round(ms * 1e3, 1),
+                     "TFLOPs": round(tf, 1), "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+    del T, Y, dX, dW
+    torch.cuda.empty_cache()
+    return res
+
+
 def quantize_only(lib, torch):
     """The quantizer alone on the 8192 x 4096 heavy-tailed activation workload
     (Student-t x normal body, 16 outlier columns x100): row-wise only and
@@ -484,48 +614,71 @@ def quantize_only(lib, torch):
     return res
 
 
-def cpu_baseline(step_flops, step_elems):
-    """The CPU oracle (as it stands) on a bounded sample of one step: the
-    quantization of 64 output rows of dY_up in both orientations (SR) and
-    the fp64 GEMM of 16 output rows of the up projection's fprop.  The step
-    time is extrapolated per element and per flop, and reported in the same
-    TFLOP/s unit as `value`."""
+def cpu_baseline(step_flops, step_elems, sample):
+    """The CPU oracle (as it stands) on a bounded sample of one step, about
+    10-20 s of host work: the stochastic-rounding quantization of 2048 output
+    rows of dY_up in each orientation (numpy, one thread) and the fp64 GEMM
+    of 1024 output rows of the up projection's fprop (numpy matmul on the
+    BLAS threads, dequantization and the tolerance bound included).  The
+    step time is extrapolated per output element and per flop and reported in
+    the same TFLOP/s unit as `value`.  `cores` is the largest number of
+    threads the sample ran on (the BLAS pool); the host's CPU count and the
+    process's affinity mask are recorded beside it."""
     import numpy as np
 
     from oracle import gemm, quantize
-    from workloads import config, sr_seed
+    from workloads import sr_seed
 
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    data = config(4)
-    dy = data["dY_up"]
+        blas = 1
+    affinity = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    dy = sample["dY_up"]
     t0 = time.perf_counter()
-    q_rows = 64
     for o, n_out in ((0, dy.shape[0]), (1, dy.shape[1])):
-        rows = np.arange(q_rows) * (n_out // q_rows)
+        rows = np.arange(CPU_QUANT_ROWS) * (n_out // CPU_QUANT_ROWS)
         quantize.quantize_blockscale(dy, np.float32(1e-7), quantize.SR, sr_seed(4), 0, o, rows=rows)
     tq = time.perf_counter() - t0
-    q_elems = 2 * q_rows * dy.shape[1]  # output elements produced (avg over orientations)
-    x = data["X"][:16]
-    w = data["W_up"]
+    q_elems = CPU_QUANT_ROWS * dy.shape[1] + CPU_QUANT_ROWS * dy.shape[0]  # output elements produced
+    x, w = sample["X_rows"], sample["W_up"]
     xc, xs = quantize.quantize_blockscale(x, np.float32(1e-4), quantize.RNE)
     wc, ws = quantize.quantize_blockscale(w, np.float32(1e-6), quantize.RNE)
     t1 = time.perf_counter()
     gemm.gemm_nt(xc, xs, 1e-4, wc, ws, 1e-6)
     tg = time.perf_counter() - t1
-    g_flops = 2.0 * 16 * w.shape[0] * w.shape[1]
+    g_flops = 2.0 * x.shape[0] * w.shape[0] * w.shape[1]
     # every input element is quantized in two orientations per step
     est_step_s = tq / q_elems * (2 * step_elems) + tg / g_flops * step_flops
     return {"value": round(step_flops / est_step_s / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"quantize (SR) of {q_rows} output rows per orientation of dY_up "
-                      f"8192x16384 ({tq:.1f} s) + fp64 fprop GEMM of 16 x 16384 x 4096 "
-                      f"({tg:.1f} s, dequantize included); step time extrapolated per element "
-                      f"and per flop: {est_step_s:.0f} s"}
+            "cores": int(blas), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "affinity_cpus": len(affinity),
+            "affinity_mask": _cpu_ranges(affinity),
+            "quantize_threads": 1, "gemm_threads": int(blas),
+            "quantize_GBps": round(q_elems * 3.125 / 2 / tq / 1e9, 4),
+            "gemm_GFLOPs": round(g_flops / tg / 1e9, 2),
+            "sample": f"quantize (SR) of {CPU_QUANT_ROWS} output rows per orientation of dY_up "
+                      f"8192x16384 ({tq:.1f} s, 1 thread) + fp64 fprop GEMM of {x.shape[0]} x 16384 x "
+                      f"4096 ({tg:.1f} s, {blas} BLAS threads, dequantize and bound included); step "
+                      f"time extrapolated per element and per flop: {est_step_s:.0f} s"}
+
+
+def _cpu_ranges(cpus):
+    """[0, 1, 2, 5] -> '0-2,5'."""
+    out, start, prev = [], None, None
+    for c in cpus:
+        if start is None:
+            start = prev = c
+        elif c == prev + 1:
+            prev = c
+        else:
+            out.append(f"{start}-{prev}" if prev > start else str(start))
+            start = prev = c
+    if start is not None:
+        out.append(f"{start}-{prev}" if prev > start else str(start))
+    return ",".join(out)
 
 
 if __name__ == "__main__":
