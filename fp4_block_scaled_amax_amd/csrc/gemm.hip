@@ -216,11 +216,14 @@ __device__ __forceinline__ int qtile_offset(int row, int col) {
 // and the pair swaps them (DPP), as in the stand-alone quantizer.  The
 // batch's LDS reads issue together, and the path check is once per batch.
 // Output row m0 + row of the M x N output, stochastic bits from orientation
-// 0 of that shape.
+// 0 of that shape.  Each unit inside the output is also written to the bf16
+// output C (a wave stores two whole 512-byte tile rows; N % 16 == 0 here) and
+// its magnitudes are folded into tmax.
 template <bool SR>
 __device__ __forceinline__ void quantize_tile_rows(const uint8_t* tile, const Ctx& ctx, const float* rlut,
                                                    const OutputQuant& q, int64_t m0, int64_t n0,
-                                                   int64_t M, int64_t N) {
+                                                   int64_t M, int64_t N, uint16_t* __restrict__ Cb,
+                                                   uint32_t& tmax) {
     const int t = threadIdx.x, u = t & 31;
     const uint32_t p = t & 1;
     const int64_t gc = n0 + 8 * u;
@@ -234,7 +237,14 @@ __device__ __forceinline__ void quantize_tile_rows(const uint8_t* tile, const Ct
             w[k] = *reinterpret_cast<const u32x4*>(tile + qtile_offset(row, 8 * u));
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) hmax[k] = max_abs8(w[k]);
+        for (int k = 0; k < 8; ++k) {
+            hmax[k] = max_abs8(w[k]);
+            const int64_t gr = m0 + (t >> 5) + 8 * (8 * batch + k);
+            if (gr < M && gc < N) {
+                *reinterpret_cast<u32x4*>(Cb + gr * N + gc) = w[k];
+                tmax = max(tmax, hmax[k]);
+            }
+        }
         uint32_t code[8];
         float rr[8];
         bool ok = ctx.fastK;
@@ -289,6 +299,39 @@ __device__ __forceinline__ void quantize_tile_rows(const uint8_t* tile, const Ct
             if (gr < M && gc < N) {
                 *reinterpret_cast<uint32_t*>(q.row_codes + gr * (N / 2) + gc / 2) = packed[k];
                 if (p == 0) q.row_scales[gr * (N / 16) + gc / 16] = (uint8_t)code[k];
+            }
+        }
+    }
+}
+
+// The bf16 output tile held in LDS written to C (used when only the
+// transposed quantization is requested, so N may be any size): thread t
+// copies 16-byte unit t % 32 of tile rows t / 32 + 8k, element by element at
+// a ragged right edge or when N % 8 != 0; the stored magnitudes are folded
+// into tmax.
+__device__ __forceinline__ void store_tile(const uint8_t* tile, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                           uint16_t* __restrict__ Cb, uint32_t& tmax) {
+    const int t = threadIdx.x, u = t & 31;
+    const int64_t gc = n0 + 8 * u;
+    const bool whole = N % 8 == 0 && gc + 8 <= N;
+#pragma unroll 4
+    for (int k = 0; k < kBM / 8; ++k) {
+        const int row = (t >> 5) + 8 * k;
+        const int64_t gr = m0 + row;
+        if (gr >= M || gc >= N) continue;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + qtile_offset(row, 8 * u));
+        if (whole) {
+            *reinterpret_cast<u32x4*>(Cb + gr * N + gc) = w;
+            tmax = max(tmax, max_abs8(w));
+        } else {
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (gc + e < N) {
+                    const uint16_t b = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
+                    Cb[gr * N + gc + e] = b;
+                    tmax = max(tmax, (uint32_t)(b & 0x7FFFu));
+                }
             }
         }
     }
@@ -559,8 +602,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const int64_t row0 = m0 + wm * 128 + 4 * h, col0 = n0 + wn * 128 + r;
     const int trow0 = wm * 128 + 4 * h, tcol0 = wn * 128 + r;  // within the tile
     uint32_t tmax = 0u;  // max |bf16| bits stored by this lane
-    if (QUANT) __syncthreads();  // every wave is done with the staging buffers
-    if (m0 + kBM <= M && n0 + kBN <= N) {
+    if (QUANT) {
+        // The bf16 tile goes to LDS only (the staging buffers are free once
+        // every wave is past its last MFMA); the passes below write it to C
+        // from there, 16 bytes per lane, and quantize it.  Values outside
+        // the output share no 16-block with stored ones (the quantized axes
+        // are multiples of 16).
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint16_t*>(
+                        smem + qtile_offset(trow0 + i * 32 + 8 * (e >> 2) + (e & 3), tcol0 + j * 32)) =
+                        to_bf16((acc[i][j][e] * sa256) * tsb);
+        float* rlut = reinterpret_cast<float*>(smem + kQTile);
+        const Ctx ctx = make_ctx(*q.ts);
+        rlut[tid] = q.stochastic ? rcp_entry<true>((uint32_t)tid, ctx.ts) : rcp_entry<false>((uint32_t)tid, ctx.ts);
+        __syncthreads();  // tile and table visible
+        if (q.row_codes) {
+            if (q.stochastic) quantize_tile_rows<true>(smem, ctx, rlut, q, m0, n0, M, N, Cb, tmax);
+            else quantize_tile_rows<false>(smem, ctx, rlut, q, m0, n0, M, N, Cb, tmax);
+        } else {
+            store_tile(smem, m0, n0, M, N, Cb, tmax);
+        }
+        if (q.col_codes) {
+            if (q.stochastic) quantize_tile_cols<true>(smem, ctx, rlut, q, m0, n0, M, N);
+            else quantize_tile_cols<false>(smem, ctx, rlut, q, m0, n0, M, N);
+        }
+    } else if (m0 + kBM <= M && n0 + kBN <= N) {
         // interior tile: one row pointer per accumulator row, the 4 column
         // tiles at immediate offsets
 #pragma unroll
@@ -575,9 +647,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
                         const uint16_t b = to_bf16(v);
                         Cb[off + j * 32] = b;
                         tmax = max(tmax, (uint32_t)(b & 0x7FFFu));
-                        if (QUANT)
-                            *reinterpret_cast<uint16_t*>(
-                                smem + qtile_offset(trow0 + i * 32 + 8 * (e >> 2) + (e & 3), tcol0 + j * 32)) = b;
                     } else {
                         C[off + j * 32] = v;
                     }
@@ -602,28 +671,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
                             C[row * N + col] = v;
                         }
                     }
-                    // outside the output: a value that shares no 16-block
-                    // with a stored one (the quantized axes are multiples of 16)
-                    if (QUANT)
-                        *reinterpret_cast<uint16_t*>(
-                            smem + qtile_offset(trow0 + i * 32 + 8 * (e >> 2) + (e & 3), tcol0 + j * 32)) =
-                            to_bf16(v);
                 }
             }
-    }
-    if (QUANT) {
-        float* rlut = reinterpret_cast<float*>(smem + kQTile);
-        const Ctx ctx = make_ctx(*q.ts);
-        rlut[tid] = q.stochastic ? rcp_entry<true>((uint32_t)tid, ctx.ts) : rcp_entry<false>((uint32_t)tid, ctx.ts);
-        __syncthreads();  // tile and table visible
-        if (q.row_codes) {
-            if (q.stochastic) quantize_tile_rows<true>(smem, ctx, rlut, q, m0, n0, M, N);
-            else quantize_tile_rows<false>(smem, ctx, rlut, q, m0, n0, M, N);
-        }
-        if (q.col_codes) {
-            if (q.stochastic) quantize_tile_cols<true>(smem, ctx, rlut, q, m0, n0, M, N);
-            else quantize_tile_cols<false>(smem, ctx, rlut, q, m0, n0, M, N);
-        }
     }
     if (BF16 && amax != nullptr) amax_commit(tmax, amax);
 }
