@@ -52,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA, MI355X
 TOKENS, HIDDEN, FFN = 8192, 4096, 16384
 QUANT_BYTES_PER_ELEM = 2.0 + 2 * 0.5625  # bf16 in; codes + scales out, both orientations
-CPU_GEMM_ROWS = 1024  # output rows of the up projection's fprop in the oracle's timed sample
-CPU_QUANT_ROWS = 2048  # output rows per orientation of dY_up in the oracle's timed sample
+CPU_GEMM_ROWS = 4096  # output rows of the up projection's fprop in the oracle's timed sample
+CPU_QUANT_ROWS = 3072  # output rows per orientation of dY_up in the oracle's timed sample
 
 
 def parse():
@@ -616,9 +616,9 @@ def quantize_only(lib, torch):
 
 def cpu_baseline(step_flops, step_elems, sample):
     """The CPU oracle (as it stands) on a bounded sample of one step, about
-    10-20 s of host work: the stochastic-rounding quantization of 2048 output
+    10-20 s of host work: the stochastic-rounding quantization of 3072 output
     rows of dY_up in each orientation (numpy, one thread) and the fp64 GEMM
-    of 1024 output rows of the up projection's fprop (numpy matmul on the
+    of 4096 output rows of the up projection's fprop (numpy matmul on the
     BLAS threads, dequantization and the tolerance bound included).  The
     step time is extrapolated per output element and per flop and reported in
     the same TFLOP/s unit as `value`.  `cores` is the largest number of
