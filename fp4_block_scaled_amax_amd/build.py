@@ -38,13 +38,15 @@ SOURCE_FLAGS = {
 
 
 def kernel_fingerprint(src):
-    """SHA-256 of a source file and the options it is compiled with: what a
-    recorded measurement of its kernels refers to."""
+    """SHA-256 of a source file, the headers beside it (every source includes
+    some of them) and the options it is compiled with: what a recorded
+    measurement of its kernels refers to."""
     import hashlib
 
     h = hashlib.sha256()
-    with open(os.path.join(CSRC, src), "rb") as f:
-        h.update(f.read())
+    for name in [src] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp")):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     h.update(repr((HIP_FLAGS, SOURCE_FLAGS.get(src, []))).encode())
     return h.hexdigest()
 

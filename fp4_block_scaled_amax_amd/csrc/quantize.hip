@@ -154,7 +154,10 @@ __global__ __launch_bounds__(1024) void amax_kernel(const uint16_t* __restrict__
 // workgroup 0 stores it to *tensor_scale.  Every workgroup computes the same
 // value, and one that reads *tensor_scale after the store reads it only in
 // the case where the store wrote back the value it found.
-template <int TR, bool ROW, bool COL, bool SR, bool AMAX>
+// W32 (stochastic rounding only): every call number of the launch is below
+// 2^32 (fewer than 2^35 elements), so the counter's second word is 0 and
+// sr_words32 applies.
+template <int TR, bool ROW, bool COL, bool SR, bool AMAX, bool W32>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     float* tensor_scale, uint64_t seed, uint32_t offset,
@@ -204,13 +207,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     // Row-only calls draw them here, while the loads are in flight; with the
     // transposed output as well, the 32 registers they would hold meanwhile
     // cost a resident workgroup, so they are drawn where they are used.
-    // When every call number of the launch is below 2^32 (fewer than 2^35
-    // elements), the counter's second word is 0 (sr_words32).
-    const bool n32 = (uint64_t)rows * (uint64_t)cols < ((uint64_t)1 << 35);
+    // With W32 the counter's second word is 0 (sr_words32).
     const uint64_t n0 = ((uint64_t)(R0 + rbase) * (uint64_t)cols + (uint64_t)c0) >> 3;
     auto row_words = [&](int k) {
         const uint64_t n = n0 + (uint64_t)k * (uint64_t)cols;
-        return n32 ? sr_words32((uint32_t)n, offset, 0u, seed) : sr_words(n, offset, 0u, seed);
+        if constexpr (W32) return sr_words32((uint32_t)n, offset, 0u, seed);
+        else return sr_words(n, offset, 0u, seed);
     };
     constexpr bool kEarlyWords = SR && ROW && !COL;
     U32x4 early[kEarlyWords ? kRowsPerThread : 1];
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             if (SR) {
                 const uint64_t na = ((uint64_t)ca * (uint64_t)rows + (uint64_t)r0) >> 3;
                 const uint64_t nb = na + (uint64_t)(rows >> 3);
-                if (n32) {
+                if constexpr (W32) {
                     rnd[0] = sr_words32((uint32_t)na, offset, 1u, seed);
                     rnd[1] = sr_words32((uint32_t)na + 1u, offset, 1u, seed);
                     rnd[2] = sr_words32((uint32_t)nb, offset, 1u, seed);
@@ -410,13 +412,24 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     if (AMAX) amax_commit(tmax, amax_inout);
 }
 
-template <bool ROW, bool COL, bool SR, bool AMAX>
-void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+// Stochastic-rounding call numbers fit 32 bits: fewer than 2^35 elements.
+bool words32(int64_t rows, int64_t cols) { return (uint64_t)rows * (uint64_t)cols < ((uint64_t)1 << 35); }
+
+template <bool ROW, bool COL, bool SR, bool AMAX, bool W32>
+void launch_quantize_w(const QuantizeArgs& a, hipStream_t stream) {
     constexpr int TR = COL ? 64 : 32;
     const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + TR - 1) / TR);
-    hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.x,
-                       a.rows, a.cols, a.ld, const_cast<float*>(a.tensor_scale), a.seed, a.offset, a.row_codes,
-                       a.row_scales, a.col_codes, a.col_scales, a.amax_inout, a.current_amax, a.max_safe);
+    hipLaunchKernelGGL((quantize_kernel<TR, ROW, COL, SR, AMAX, W32>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, a.x, a.rows, a.cols, a.ld, const_cast<float*>(a.tensor_scale), a.seed, a.offset,
+                       a.row_codes, a.row_scales, a.col_codes, a.col_scales, a.amax_inout, a.current_amax, a.max_safe);
+}
+
+template <bool ROW, bool COL, bool SR, bool AMAX>
+void launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+    if constexpr (SR) {
+        if (words32(a.rows, a.cols)) return launch_quantize_w<ROW, COL, SR, AMAX, true>(a, stream);
+    }
+    launch_quantize_w<ROW, COL, SR, AMAX, false>(a, stream);
 }
 
 // Compute units of the current device (the runtime caches the attribute).
@@ -487,7 +500,7 @@ __device__ __forceinline__ void transpose_nibbles8(uint32_t (&w)[8]) {
 constexpr int k2dRows = 64;   // tile rows: 4 waves x 16
 constexpr int k2dWords = 33;  // LDS words per tile row of packed codes (32 + 1: conflict-free columns)
 
-template <bool ROW, bool COL, bool SR, bool AMAX>
+template <bool ROW, bool COL, bool SR, bool AMAX, bool W32>
 __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ tensor_scale, uint64_t seed, uint32_t offset,
@@ -525,12 +538,12 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
         }
     }
     // stochastic rounding: call n of row rb + 2k is n0 + k * cols / 4; the
-    // counter's second word is 0 when every call number is below 2^32
-    const bool n32 = (uint64_t)rows * (uint64_t)cols < ((uint64_t)1 << 35);
+    // counter's second word is 0 when every call number is below 2^32 (W32)
     const uint64_t n0 = ((uint64_t)rb * (uint64_t)cols + (uint64_t)c0) >> 3;
     auto row_words = [&](int k) {
         const uint64_t n = n0 + (uint64_t)k * (uint64_t)(cols >> 2);
-        return n32 ? sr_words32((uint32_t)n, offset, 0u, seed) : sr_words(n, offset, 0u, seed);
+        if constexpr (W32) return sr_words32((uint32_t)n, offset, 0u, seed);
+        else return sr_words(n, offset, 0u, seed);
     };
 
     Ctx ctx;
@@ -640,12 +653,20 @@ __global__ __launch_bounds__(kThreads) void quantize2d_kernel(
     if (AMAX) amax_commit(tmax, amax_inout);
 }
 
-template <bool ROW, bool COL, bool SR, bool AMAX>
-void launch_quantize2d_t(const QuantizeArgs& a, hipStream_t stream) {
+template <bool ROW, bool COL, bool SR, bool AMAX, bool W32>
+void launch_quantize2d_w(const QuantizeArgs& a, hipStream_t stream) {
     const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + k2dRows - 1) / k2dRows);
-    hipLaunchKernelGGL((quantize2d_kernel<ROW, COL, SR, AMAX>), dim3((unsigned)tiles), dim3(kThreads), 0,
+    hipLaunchKernelGGL((quantize2d_kernel<ROW, COL, SR, AMAX, W32>), dim3((unsigned)tiles), dim3(kThreads), 0,
                        stream, a.x, a.rows, a.cols, a.ld, a.tensor_scale, a.seed, a.offset, a.row_codes,
                        a.row_scales, a.col_codes, a.col_scales, a.amax_inout);
+}
+
+template <bool ROW, bool COL, bool SR, bool AMAX>
+void launch_quantize2d_t(const QuantizeArgs& a, hipStream_t stream) {
+    if constexpr (SR) {
+        if (words32(a.rows, a.cols)) return launch_quantize2d_w<ROW, COL, SR, AMAX, true>(a, stream);
+    }
+    launch_quantize2d_w<ROW, COL, SR, AMAX, false>(a, stream);
 }
 
 template <bool ROW, bool COL>
