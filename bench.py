@@ -233,6 +233,29 @@ def main():
         return {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "avg_launch_ms": round(ms / len(sel), 4), "launches_per_step": len(sel) // args.steps}
 
+    # the streaming reference (same bytes, contiguous streams, no arithmetic)
+    # on the step's six tensors in the step's order: the HBM rate each
+    # rounding's quantize calls could reach with their read/write mix
+    ref_ms = {lib.RNE: [], lib.SR: []}
+    for p in range(4):
+        evs = []
+        for t in tensors:
+            e0, e1 = ev(), ev()
+            e0.record()
+            lib.stream_reference(t.x, t.row, t.col)
+            e1.record()
+            evs.append((e0, e1, t.rounding))
+        torch.cuda.synchronize()
+        if p > 0:  # the first pass is a warm-up
+            for e0, e1, rnd in evs:
+                ref_ms[rnd].append(e0.elapsed_time(e1))
+
+    def with_reference(stats, rounding):
+        ref = float(np.mean(ref_ms[rounding]))
+        stats["stream_reference_avg_launch_ms"] = round(ref, 4)
+        stats["frac_of_stream_reference"] = round(ref / stats["avg_launch_ms"], 4)
+        return stats
+
     traffic = gemm_traffic()
 
     result = {
@@ -263,7 +286,8 @@ def main():
                      "flop_per_launch": gemm_fl[0],
                      "traffic": None if traffic is None else round(traffic)},
         "quantize": {"peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_elem": QUANT_BYTES_PER_ELEM,
-                     "rne": q_stats(lib.RNE), "sr": q_stats(lib.SR)},
+                     "rne": with_reference(q_stats(lib.RNE), lib.RNE),
+                     "sr": with_reference(q_stats(lib.SR), lib.SR)},
     }
     step_elems = sum(t.elems for t in tensors)
     if not args.no_graph:
@@ -555,7 +579,11 @@ def quantize_only(lib, torch):
     the 2-D (16 x 16 tile) variant, both outputs from one rounding.
     8 device copies of the input and 8 output sets rotate (about 840 MB) so
     every launch reads and writes HBM, not the 256 MB cache.  GB/s counts the
-    algorithmic bytes: 2 per element read, 0.5625 per element per output."""
+    algorithmic bytes: 2 per element read, 0.5625 per element per output.
+    The streaming reference (a kernel that moves the same bytes as contiguous
+    streams, no quantization) is timed on the same buffers: each variant's
+    frac_of_stream_reference is its time against that, the share of the HBM
+    rate its read/write mix can reach that it reaches."""
     from workloads import config, sr_seed
 
     bits = config(2)["X"]
@@ -579,10 +607,14 @@ def quantize_only(lib, torch):
                                      ("sr_row_col", lib.SR, True, False),
                                      ("current_scaling_rne_row_col", lib.RNE, True, True),
                                      ("tile2d_rne_row_col", lib.RNE, True, False),
-                                     ("tile2d_sr_row_col", lib.SR, True, False)):
+                                     ("tile2d_sr_row_col", lib.SR, True, False),
+                                     ("stream_reference_row", None, False, False),
+                                     ("stream_reference_row_col", None, True, False)):
         def run(i):
             k = i % sets
-            if name.startswith("tile2d"):
+            if name.startswith("stream_reference"):
+                lib.stream_reference(xs[k], outs[k][0], outs[k][1] if both else None)
+            elif name.startswith("tile2d"):
                 lib.quantize_blockscale_2d(xs[k], ts, rnd, sr_seed(2), i, row=outs[k][0], col=outs[k][1],
                                            amax=amax)
             elif current:
@@ -611,6 +643,10 @@ def quantize_only(lib, torch):
     cur = res["current_scaling_rne_row_col"]
     cur["extra_read_bytes"] = rows * cols * 2
     cur["time_vs_periodic"] = round(cur["us"] / res["rne_row_col"]["us"], 3)
+    for name, r in res.items():
+        if isinstance(r, dict) and not name.startswith("stream_reference"):
+            ref = res["stream_reference_row_col" if "row_col" in name else "stream_reference_row"]
+            r["frac_of_stream_reference"] = round(ref["us"] / r["us"], 4)
     return res
 
 

@@ -48,6 +48,7 @@ _SIGNATURES = {
     "ue5m3fp4_quantize_current_scaling": [_c_void_p, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
                                           ctypes.c_uint64, ctypes.c_uint32, _c_void_p, _c_void_p,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "ue5m3fp4_stream_reference": [_c_void_p, _i64] + [_c_void_p] * 5,
 }
 
 _lib = None
@@ -251,6 +252,34 @@ def dequantize(q, out, stream=None):
                                             q.cols, _ptr(out), _stream(stream))
     _check(st, "ue5m3fp4_dequantize")
     return out
+
+
+def stream_reference(x, row, col=None, stream=None):
+    """Measurement aid (no quantization): the byte traffic of a quantize call
+    on x (bf16 [R][C], contiguous) as contiguous streams into the code and
+    scale buffers of `row` (and `col`), each a (codes, scales) pair or a
+    Quantized of the matching shape.  Its time is the HBM rate the
+    quantizer's read/write mix can reach."""
+    import torch
+
+    _require(x, (torch.bfloat16, torch.int16, torch.uint16), "x", 2, contiguous=True)
+    rows, cols = x.shape
+    if cols % 16 != 0:
+        raise ValueError("x: cols must be a multiple of 16")
+    pairs = []
+    for name, out, r, c in (("row", row, rows, cols), ("col", col, cols, rows)):
+        if out is None:
+            pairs.append((None, None))
+            continue
+        codes, scales = (out.codes, out.scales) if isinstance(out, Quantized) else out
+        _check_pair(codes, scales, r, c, name)
+        _same_device("stream_reference", x, codes)
+        pairs.append((codes, scales))
+    if pairs[0][0] is None:
+        raise ValueError("row is required")
+    st = load_library().ue5m3fp4_stream_reference(_ptr(x), rows * cols, _ptr(pairs[0][0]), _ptr(pairs[0][1]),
+                                                  _ptr(pairs[1][0]), _ptr(pairs[1][1]), _stream(stream))
+    _check(st, "ue5m3fp4_stream_reference")
 
 
 def _gemm_out(out, m, n, dtypes=None):

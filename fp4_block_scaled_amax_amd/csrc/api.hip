@@ -189,6 +189,19 @@ int ue5m3fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float
     return launch_status();
 }
 
+int ue5m3fp4_stream_reference(const uint16_t* x, int64_t elems, uint8_t* codes0, uint8_t* scales0,
+                              uint8_t* codes1, uint8_t* scales1, void* stream) {
+    if (elems < 0) return UE5M3FP4_EINVAL;
+    if (elems % 16 != 0) return UE5M3FP4_ESHAPE;
+    if (elems >= kMaxElems) return UE5M3FP4_ERANGE;
+    if (elems == 0) return UE5M3FP4_OK;
+    if (!x || !codes0 || !scales0 || (codes1 == nullptr) != (scales1 == nullptr)) return UE5M3FP4_EINVAL;
+    if (!aligned16(x) || !aligned16(codes0) || (codes1 && !aligned16(codes1))) return UE5M3FP4_EALIGN;
+    clear_stale_error();
+    launch_stream_reference(x, elems, codes0, scales0, codes1, scales1, (hipStream_t)stream);
+    return launch_status();
+}
+
 int ue5m3fp4_gemm_nt(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
                      int64_t M, int64_t N, int64_t K, float* c, void* stream) {

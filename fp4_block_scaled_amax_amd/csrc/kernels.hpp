@@ -37,6 +37,11 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float*
 void launch_update_tensor_scale(float* amax_running, float* tensor_scale, float max_safe,
                                 hipStream_t stream);
 
+// Streaming reference of a quantize call's traffic (elems % 16 == 0; codes1
+// and scales1 both null for one output).
+void launch_stream_reference(const uint16_t* x, int64_t elems, uint8_t* codes0, uint8_t* scales0,
+                             uint8_t* codes1, uint8_t* scales1, hipStream_t stream);
+
 // *p = 0 (the running amax before a current-tensor-scaling amax pass).
 void launch_zero_scalar(float* p, hipStream_t stream);
 

@@ -449,6 +449,28 @@ void launch_amax(const QuantizeArgs& a, hipStream_t s) {
                        a.amax_inout);
 }
 
+// Streaming reference (measurement only, no quantization arithmetic): the
+// byte traffic of a quantize call as contiguous streams -- per 16-element
+// block, 32 bytes read, then 8 bytes of "codes" and 1 "scale" byte written
+// per output (the codes are XORs of the input words).  Its time is what HBM
+// gives for the quantizer's read/write mix without the quantizer's access
+// pattern or arithmetic.
+__global__ __launch_bounds__(256) void stream_reference_kernel(const u32x4* __restrict__ x, int64_t blocks,
+                                                               u32x2* __restrict__ c0, uint8_t* __restrict__ s0,
+                                                               u32x2* __restrict__ c1, uint8_t* __restrict__ s1) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < blocks; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(x + 2 * i), b = __builtin_nontemporal_load(x + 2 * i + 1);
+        const uint32_t h = a.x ^ a.y ^ a.z ^ a.w, g = b.x ^ b.y ^ b.z ^ b.w;
+        __builtin_nontemporal_store(u32x2{h, g}, c0 + i);
+        s0[i] = (uint8_t)(h ^ g);
+        if (c1 != nullptr) {
+            __builtin_nontemporal_store(u32x2{g, h}, c1 + i);
+            s1[i] = (uint8_t)((h ^ g) >> 8);
+        }
+    }
+}
+
 template <bool ROW, bool COL, bool SR>
 void dispatch_amax(const QuantizeArgs& a, hipStream_t s) {
     if (a.amax_inout) launch_quantize<ROW, COL, SR, true>(a, s);
@@ -753,6 +775,15 @@ void launch_quantize_2d(const QuantizeArgs& a, hipStream_t s) {
     if (row && col) dispatch_2d<true, true>(a, s);
     else if (row) dispatch_2d<true, false>(a, s);
     else dispatch_2d<false, true>(a, s);
+}
+
+void launch_stream_reference(const uint16_t* x, int64_t elems, uint8_t* codes0, uint8_t* scales0,
+                             uint8_t* codes1, uint8_t* scales1, hipStream_t s) {
+    const int64_t blocks = elems / 16;
+    const int64_t grid = max((int64_t)1, min((blocks + 255) / 256, (int64_t)cu_count() * 32));
+    hipLaunchKernelGGL(stream_reference_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(x), blocks, reinterpret_cast<u32x2*>(codes0), scales0,
+                       reinterpret_cast<u32x2*>(codes1), scales1);
 }
 
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,

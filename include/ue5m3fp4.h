@@ -280,6 +280,21 @@ UE5M3FP4_API int ue5m3fp4_update_tensor_scale(float* amax_running, float* tensor
                                  int64_t period, float max_safe, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
+/* Measurement aid, not part of the method (it does no quantization): moves
+ * the bytes of a quantize call as contiguous streams, so that its time is
+ * the HBM rate available to the quantizer's read/write mix.  Reads x, elems
+ * bf16 values (elems % 16 == 0, contiguous); per 16-value block writes 8
+ * bytes to codes0 and 1 byte to scales0 (buffers of elems/2 and elems/16
+ * bytes), and the same to codes1 / scales1 when both are non-NULL (one pair
+ * NULL and the other not: UE5M3FP4_EINVAL).  Byte 0..7 of block i's codes
+ * hold the XOR of words 0..3 and of words 4..7 of the block (little-endian
+ * u32 pair; codes1 holds the pair swapped); scales0 byte i is the low byte of
+ * their XOR, scales1 byte i the next byte.  x and codes 16-byte aligned
+ * (UE5M3FP4_EALIGN), NULL x / codes0 / scales0 UE5M3FP4_EINVAL, elems < 0
+ * UE5M3FP4_EINVAL, elems % 16 != 0 UE5M3FP4_ESHAPE. */
+UE5M3FP4_API int ue5m3fp4_stream_reference(const uint16_t* x, int64_t elems, uint8_t* codes0, uint8_t* scales0,
+                                           uint8_t* codes1, uint8_t* scales1, void* stream);
+
 UE5M3FP4_API const char* ue5m3fp4_status_string(int status);
 
 #ifdef __cplusplus

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     # and only those: internal C++ symbols stay hidden
@@ -212,3 +212,16 @@ def test_binding_requires_built_library(tmp_path):
             lib.load_library(str(tmp_path / "nope.so"))
         finally:
             lib._lib = saved
+
+
+def test_stream_reference_checks(L):
+    sr = L.ue5m3fp4_stream_reference
+    assert sr(P, 24, P, P, None, None, None) == ESHAPE
+    assert sr(P, -16, P, P, None, None, None) == EINVAL
+    assert sr(None, 16, P, P, None, None, None) == EINVAL
+    assert sr(P, 16, P, None, None, None, None) == EINVAL
+    assert sr(P, 16, P, P, P, None, None) == EINVAL       # one of the second pair
+    assert sr(M4, 16, P, P, None, None, None) == EALIGN
+    assert sr(P, 16, P, P, M4, P, None) == EALIGN
+    assert sr(P, 1 << 40, P, P, None, None, None) == ERANGE
+    assert sr(None, 0, None, None, None, None, None) == OK

@@ -150,3 +150,14 @@ def test_quantizing_epilogue_checks():
     raises(lambda: lib.gemm_nt_bf16_quantized(a, b, out, torch.ones(1), row=operand(32, 48)), "device")
     raises(lambda: lib.gemm_nt_bf16_quantized(a, b, out, ts, row=operand(48, 32)))
     raises(lambda: lib.gemm_nt_bf16_quantized(a, b, out, ts, col=lib.Quantized(u8(48, 32)[:, ::2], u8(48, 2), ts)))
+
+
+def test_stream_reference_checks():
+    x = Dev(torch.zeros((32, 64), dtype=torch.bfloat16))
+    good_r, good_c = (u8(32, 32), u8(32, 4)), (u8(64, 16), u8(64, 2))
+    raises(lambda: lib.stream_reference(x, None), "row is required")
+    raises(lambda: lib.stream_reference(Dev(torch.zeros((32, 40), dtype=torch.bfloat16)), good_r), "multiple of 16")
+    raises(lambda: lib.stream_reference(torch.zeros((32, 64), dtype=torch.bfloat16), good_r), "device")
+    raises(lambda: lib.stream_reference(x, (u8(32, 16), u8(32, 4))), "do not match")
+    raises(lambda: lib.stream_reference(x, good_r, (u8(32, 32), u8(32, 4))), "do not match")
+    raises(lambda: lib.stream_reference(x[:, ::2], good_r), "contiguous")
