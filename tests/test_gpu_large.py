@@ -7,7 +7,10 @@ oracle on the generator's block (round to nearest: the codes do not depend
 on coordinates, so a sampled row can be quantized on its own).
 
 Sizes: x is 133120 x 16384 bf16 (2.18e9 elements, 4.4 GB; outputs 1.2 GB per
-orientation); C is 65536 x 36864 fp32 (2.4e9 entries, 9.7 GB)."""
+orientation); C is 65536 x 36864 fp32 (2.4e9 entries, 9.7 GB).  Past 2^35
+elements (below) the stochastic-rounding counters take their 64-bit form:
+there x is 133120 x 262144 (69.8 GB), checked through the 1-D and the 2-D
+quantizer."""
 
 import numpy as np
 import pytest
@@ -103,4 +106,83 @@ def test_gemm_output_past_2_31_entries(cuda_device):
     ref, bound = ogemm.gemm_nt_entries(ac, asc, 0.5, bc, bsc, 0.25, rows, cols)
     assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-5 * bound)
     del c
+    torch.cuda.empty_cache()
+
+
+# Past 2^35 elements the stochastic-rounding call numbers (element index / 8)
+# no longer fit 32 bits: the kernels take the 64-bit counter form there.
+# x is a generator block of BR x BC tiled on the device to R35 x C35
+# (3.49e10 elements, 69.8 GB; outputs 19.6 GB per orientation).  Sampled
+# output rows lie on both sides of the first call number with a nonzero high
+# word (row 131072 of the row-wise output, column 258112 of the transposed
+# one) and are compared with the oracle's row step on their own data and
+# true coordinates.
+R35, C35 = 133120, 262144
+BR, BC = 1021, 8208
+ROWS35 = [0, 1, 131071, 131072, 131073, R35 - 1]
+COLS35 = [0, 7, 258111, 258112, 258113, C35 - 1]
+
+
+@pytest.fixture(scope="module")
+def big35(cuda_device):
+    import torch
+
+    assert R35 * C35 > 2**35 and (R35 * C35 - 8) // 8 >= 2**32
+    block = random_bf16((BR, BC), seed=20261)
+    wide = dev_bf16(block).repeat(1, -(-C35 // BC))[:, :C35].contiguous()  # BR x C35
+    x = torch.empty((R35, C35), dtype=torch.int16, device="cuda")
+    for r in range(0, R35, BR):
+        x[r:r + BR] = wide[:min(BR, R35 - r)]
+    del wide
+    ts_val = np.float32(np.float32(quantize.tensor_amax(block)) / np.float32(43008.0))
+    yield block, x, ts_val
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_stochastic_rounding_past_2_35_elements(big35):
+    import torch
+    from oracle import formats
+
+    block, x, ts_val = big35
+    ts = dev_scalar(ts_val)
+    seed, offset = 0x1234_5678_9ABC_DEF0, 77
+    qr = lib.empty_quantized(R35, C35, ts)
+    qc = lib.empty_quantized(C35, R35, ts)
+    lib.quantize_blockscale(x, ts, lib.SR, seed, offset, row=qr, col=qc)
+    torch.cuda.synchronize()
+    rows = np.array(ROWS35, dtype=np.int64)
+    cols = np.array(COLS35, dtype=np.int64)
+    # output rows of orientation 0: rows of x; of orientation 1: columns of x
+    xr = block[rows % BR][:, np.arange(C35) % BC]
+    xc = block[:, cols % BC][np.arange(R35) % BR].T
+    for orient, data, ids, q in ((0, xr, rows, qr), (1, xc, cols, qc)):
+        c, s = quantize._quantize_rows(formats.bf16_to_f32(data), ts_val, quantize.SR, seed, offset, orient,
+                                       data.shape[1], ids)
+        assert np.array_equal(host(q.scales[ids.tolist()]), s), f"scales, orientation {orient}"
+        assert np.array_equal(host(q.codes[ids.tolist()]), c), f"codes, orientation {orient}"
+    del qr, qc
+    torch.cuda.empty_cache()
+
+
+def test_stochastic_rounding_2d_past_2_35_elements(big35):
+    import torch
+
+    block, x, ts_val = big35
+    ts = dev_scalar(ts_val)
+    seed, offset = 0x0FED_CBA9_8765_4321, 5
+    qr = lib.empty_quantized(R35, C35, ts)
+    qc = lib.empty_quantized(C35, R35, ts)
+    lib.quantize_blockscale_2d(x, ts, lib.SR, seed, offset, row=qr, col=qc)
+    torch.cuda.synchronize()
+    # 16-row groups: 8191 ends just below the first call number past 2^32
+    # (row 131072), 8192 starts there
+    for g in (0, 8191, 8192, R35 // 16 - 1):
+        xs = block[(16 * g + np.arange(16)) % BR][:, np.arange(C35) % BC]
+        rc, rs, cc, cs, _ = quantize2d.quantize_blockscale_2d(xs, ts_val, quantize.SR, seed, offset, row0=16 * g)
+        assert np.array_equal(host(qr.codes[16 * g:16 * g + 16]), rc), f"row codes, group {g}"
+        assert np.array_equal(host(qr.scales[16 * g:16 * g + 16]), rs), f"row scales, group {g}"
+        assert np.array_equal(host(qc.codes[:, 8 * g:8 * g + 8]), cc), f"col codes, group {g}"
+        assert np.array_equal(host(qc.scales[:, g:g + 1]), cs), f"col scales, group {g}"
+    del qr, qc
     torch.cuda.empty_cache()
