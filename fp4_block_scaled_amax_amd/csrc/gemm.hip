@@ -440,16 +440,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     // ---- staging: global -> registers -> LDS.  Every load is unconditional
     // (rows clamped into the operand, K offsets into the row); rows outside
     // the operand and blocks past K get scale byte 0, whose factor m = 0 makes
-    // them dequantize to exactly 0.  Thread tid stages 16-byte units
-    // tid + 256 i (i = 0..3) of each operand's 256 x 64 code bytes (row
-    // unit / 4, part unit % 4) and the 8 scale bytes of row tid.  The staging
-    // registers are plain vector values (no arrays), so they stay in VGPRs.
+    // them dequantize to exactly 0.  Thread tid stages 16-byte part tid % 4 of
+    // rows srow + 64 i (i = 0..3) of each operand's 256 x 64 code bytes, and
+    // the 8 scale bytes of row tid.  A wave stores 16 rows, 4 rows x 4 parts
+    // per 16 lanes.  The LDS takes each 8-byte half of such a store 16 lanes
+    // per cycle over 32 four-byte banks (measured: the bank-conflict count
+    // follows this model exactly); at the 18-dword row stride rows o, o + 1,
+    // o + 8 and o + 9 start 0, 18, 16 and 2 banks apart, so a 16-lane group
+    // holding them writes each bank once, where 4 consecutive rows put two
+    // dwords on half the banks.  A wave still loads 16 whole 64-byte row
+    // chunks from global memory.  The staging registers are plain vector
+    // values (no arrays), so they stay in VGPRs.
     u32x4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
     u32x2 rsa, rsb;
     u32x8 ea, eb;
     const bool a_valid = m0 + tid < M, b_valid = n0 + tid < N;
     const int64_t a_srow = a_valid ? m0 + tid : M - 1, b_srow = b_valid ? n0 + tid : N - 1;
-    const int srow = tid >> 2, spart = tid & 3;  // unit tid + 256 i: row srow + 64 i
+    const int sq = (tid >> 2) & 15, spart = tid & 3;  // rows srow + 64 i, part spart
+    const int srow = 16 * (tid >> 6) + 2 * (sq >> 2) + (sq & 1) + 8 * ((sq >> 1) & 1);
     const uint8_t* a_rows[4];
     const uint8_t* b_rows[4];
 #pragma unroll
