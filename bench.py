@@ -19,7 +19,11 @@ command, reported only while the GEMM source still matches the one profiled.
 `quantize` reports the quantizer's GB/s inside the step (round-to-nearest
 and stochastic calls separately) and, as `quantize_activations`, on its own
 over the 8192 x 4096 heavy-tailed activation workload with 8 rotating
-HBM-resident buffer sets (the quantizer's bandwidth roofline).
+HBM-resident buffer sets (the quantizer's bandwidth roofline).  Both carry
+`frac_of_stream_reference`: the time of a kernel that moves the same bytes as
+contiguous streams with no quantization, over the quantizer's time -- the
+share of the HBM rate the quantizer's read/write mix can reach that it
+reaches.
 `epilogue_fusion` times the largest fprop of the step with its output fused
 for the next layer (bf16 Y and its amax) against the fp32 output.
 `native_mxfp4` times the native MXFP4 comparison GEMM at the step's GEMM

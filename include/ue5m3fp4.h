@@ -279,7 +279,6 @@ UE5M3FP4_API int ue5m3fp4_gemm_wgrad(const uint8_t* dyt_codes, const uint8_t* dy
 UE5M3FP4_API int ue5m3fp4_update_tensor_scale(float* amax_running, float* tensor_scale, int64_t step,
                                  int64_t period, float max_safe, void* stream);
 
-/* Static, NUL-terminated description of a status code. */
 /* Measurement aid, not part of the method (it does no quantization): moves
  * the bytes of a quantize call as contiguous streams, so that its time is
  * the HBM rate available to the quantizer's read/write mix.  Reads x, elems
@@ -291,10 +290,12 @@ UE5M3FP4_API int ue5m3fp4_update_tensor_scale(float* amax_running, float* tensor
  * u32 pair; codes1 holds the pair swapped); scales0 byte i is the low byte of
  * their XOR, scales1 byte i the next byte.  x and codes 16-byte aligned
  * (UE5M3FP4_EALIGN), NULL x / codes0 / scales0 UE5M3FP4_EINVAL, elems < 0
- * UE5M3FP4_EINVAL, elems % 16 != 0 UE5M3FP4_ESHAPE. */
+ * UE5M3FP4_EINVAL, elems % 16 != 0 UE5M3FP4_ESHAPE, elems >= 2^40
+ * UE5M3FP4_ERANGE. */
 UE5M3FP4_API int ue5m3fp4_stream_reference(const uint16_t* x, int64_t elems, uint8_t* codes0, uint8_t* scales0,
                                            uint8_t* codes1, uint8_t* scales1, void* stream);
 
+/* Static, NUL-terminated description of a status code. */
 UE5M3FP4_API const char* ue5m3fp4_status_string(int status);
 
 #ifdef __cplusplus
