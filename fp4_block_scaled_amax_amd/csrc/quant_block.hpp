@@ -170,9 +170,10 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], const U32x4& rn
     // 1 or 2), F is then exact, and with a seed whose high 16 bits are
     // 65535 - u and whose next two bits are set, the instruction rounds up
     // iff ceil(65536 f) > u, i.e. iff u < 65536 f -- for every v, tiny ones
-    // included (checked on gfx950 for both slots against the integer form of
-    // the definition, every 2^-17 step of |v| up to 6.5 and past it, all
-    // 65536 values of u on a third of them).  The rounding up is
+    // included (checked on gfx950 for both slots and both signs against the
+    // integer form of the definition: every 2^-17 step of |v| up to 6.5 with
+    // every third value of u, and every value of u below |v| = 0.52).  The
+    // rounding up is
     // ceil(|x r 2^17|) with x's sign, and the scale operand 2^17 undoes the
     // 2^17.  Each element takes one instruction (the two slots read
     // overlapping seed bits, so one instruction cannot round two elements
