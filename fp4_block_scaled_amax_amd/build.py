@@ -37,16 +37,43 @@ SOURCE_FLAGS = {
 }
 
 
+def _code_only(text):
+    """C++ source text without comments and with runs of white space folded:
+    what the compiler sees, so that editing a comment leaves the fingerprint
+    alone.  String and character literals are kept whole."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_fingerprint(src):
-    """SHA-256 of a source file, the headers beside it (every source includes
-    some of them) and the options it is compiled with: what a recorded
-    measurement of its kernels refers to."""
+    """SHA-256 of a source file's code, the code of the headers beside it
+    (every source includes some of them) and the options it is compiled
+    with: what a recorded measurement of its kernels refers to.  Comments
+    and white space do not count."""
     import hashlib
 
     h = hashlib.sha256()
     for name in [src] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp")):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     h.update(repr((HIP_FLAGS, SOURCE_FLAGS.get(src, []))).encode())
     return h.hexdigest()
 
