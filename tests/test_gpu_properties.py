@@ -16,7 +16,10 @@ benchmark times is checked against another launch:
 - GEMM: doubling tsA doubles C exactly (the epilogue is (acc * 256 tsA) *
   tsB); reversing the order of A's (or B's) 32-row groups, which keeps every
   row's place inside its 32 x 32 MFMA block but moves it to other tiles and
-  XCDs, permutes C's rows (columns) the same way, bit for bit.
+  XCDs, permutes C's rows (columns) the same way, bit for bit;
+- 2-D (16 x 16 tile) scales: each element is rounded once, so the transposed
+  codes are the row-wise codes transposed and both scale outputs repeat the
+  tile scale (both roundings).
 
 Inputs: config 4's X (8192 x 4096), W_up (16384 x 4096) and dY_up
 (8192 x 16384), the tensor scale refreshed from each tensor's amax.
@@ -158,3 +161,30 @@ def test_gemm_tile_permutation_whole_output(up_operands, operand):
         bp = lib.Quantized(b.codes[idx].contiguous(), b.scales[idx].contiguous(), b.ts)
         lib.gemm_nt(a, bp, cp)
         assert same(cp, c[:, idx])
+
+
+def _unpack(codes):
+    """[R][C/2] packed nibbles (element 2j low) -> [R][C] uint8 codes."""
+    import torch
+
+    return torch.stack((codes & 0x0F, codes >> 4), dim=2).reshape(codes.shape[0], -1)
+
+
+@pytest.mark.parametrize("rounding", [lib.RNE, lib.SR])
+def test_2d_transposed_output_is_the_transpose_whole_output(c4, rounding):
+    """2-D (16 x 16 tile) scales round each element once: the transposed
+    codes are the row-wise codes transposed, and both scale outputs repeat
+    the tile scale (dY_up, 8192 x 16384)."""
+    import torch
+
+    bits = c4["dY_up"]
+    R, C = bits.shape
+    ts = dev_scalar(fresh_ts(bits))
+    x = dev_bf16(bits)
+    qr, qc = lib.empty_quantized(R, C, ts), lib.empty_quantized(C, R, ts)
+    lib.quantize_blockscale_2d(x, ts, rounding, sr_seed(4), 21, row=qr, col=qc)
+    del x
+    assert same(_unpack(qc.codes), _unpack(qr.codes).t().contiguous())
+    tiles = qr.scales[::16]                                           # [R/16][C/16]
+    assert same(qr.scales, tiles.repeat_interleave(16, dim=0))
+    assert same(qc.scales, tiles.t().contiguous().repeat_interleave(16, dim=0))
