@@ -29,7 +29,8 @@ for the next layer (bf16 Y and its amax) against the fp32 output.
 `native_mxfp4` times the native MXFP4 comparison GEMM at the step's GEMM
 shape: its ratio to the UE5M3 GEMM is the cost of emulating UE5M3 scales.
 `configs` reports the other workloads call by call: the tiny linear's
-latency next to the oracle's seconds (256 x 256), the attention-projection
+latency, eager and as HIP graph replays, next to the oracle's seconds
+(256 x 256), the attention-projection
 layer (8192 x 4096 x 4096) and the dynamic-range stress layer at 4096^3 with
 stale tensor scales -- each quantization in GB/s, each GEMM in TFLOP/s.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step
@@ -478,13 +479,35 @@ def _event_ms(torch, fn, reps, warm=2):
     return e0.elapsed_time(e1) / reps
 
 
+def _graph_us(torch, fn, reps):
+    """Mean us per replay of fn(0) captured once as a HIP graph
+    (torch.cuda.graph), or a string when capture is unavailable."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn(0)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    except Exception as ex:  # capture unsupported by this runtime: report, do not fail the run
+        return f"unavailable: {type(ex).__name__}: {ex}"[:200]
+
+
 def config1_latency(lib, torch):
     """The tiny linear (X and W 256 x 256 ~N(0,1) from seed 0, tensor scales
     refreshed from their own amax, round to nearest): one pass of the path --
     amax pass and refresh per tensor, row-wise quantization of X and W,
     fprop (7 launches) -- timed on the GPU with HIP events (latency-bound,
-    no roofline claim), and the oracle's seconds for the same pass on the
-    host."""
+    no roofline claim), eagerly and as replays of the pass captured once as
+    a HIP graph (whose output must equal the eager pass's), and the oracle's
+    seconds for the same pass on the host."""
     import numpy as np
 
     from oracle import gemm, quantize, tensor_scale
@@ -505,6 +528,10 @@ def config1_latency(lib, torch):
         lib.gemm_fprop(q["X"], q["W"], y)
 
     ms = _event_ms(torch, one_pass, 50, warm=5)
+    y_eager = y.clone()
+    graph = _graph_us(torch, one_pass, 50)
+    if isinstance(graph, float):
+        graph = {"gpu_us_per_pass": round(graph, 2), "output_equals_eager": bool(torch.equal(y, y_eager))}
     t0 = time.perf_counter()
     ops = {}
     for k in ("X", "W"):
@@ -514,7 +541,7 @@ def config1_latency(lib, torch):
     oracle_s = time.perf_counter() - t0
     return {"workload": "X, W 256x256 ~N(0,1) seed 0: amax + refresh + RNE row-wise quantize of X and W, "
                         "fprop 256x256x256",
-            "gpu_us_per_pass": round(ms * 1e3, 2), "launches_per_pass": 7,
+            "gpu_us_per_pass": round(ms * 1e3, 2), "launches_per_pass": 7, "graph_replay": graph,
             "oracle_s_per_pass": round(oracle_s, 4), "bound": "latency"}
 
 
