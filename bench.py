@@ -431,8 +431,10 @@ def dynamic_range_stress(lib, torch):
     over 2^-24..2^12 per row block) quantized row-wise under a fresh tensor
     scale and under scales from an amax off by x8 and x1/8 (a stale periodic
     scale): fraction of blocks flushed to scale 0 although non-zero, of
-    blocks with a subnormal UE5M3 scale, of saturated (0xFE) blocks, and the
-    relative L2 error of the dequantized tensor.  X with round to nearest,
+    blocks with a subnormal UE5M3 scale, of saturated (0xFE) blocks, the
+    relative L2 error of the dequantized tensor (which its largest blocks
+    dominate), and the mean and median over non-zero blocks of each block's
+    own relative L2 error (1 for a flushed block).  X with round to nearest,
     dY with stochastic rounding."""
     from workloads import STALE_FACTORS, config, sr_seed
 
@@ -454,11 +456,15 @@ def dynamic_range_stress(lib, torch):
             lib.dequantize(q, out)
             sc = q.scales
             err = torch.linalg.vector_norm(out - xf) / torch.linalg.vector_norm(xf)
+            blk_err = torch.linalg.vector_norm((out - xf).view(R, C // 16, 16), dim=2)
+            blk_rel = (blk_err / torch.linalg.vector_norm(xf.view(R, C // 16, 16), dim=2))[blk_nonzero]
             entry[label] = {
                 "flushed_frac": round(float(((sc == 0) & blk_nonzero).float().mean()), 5),
                 "subnormal_scale_frac": round(float(((sc > 0) & (sc < 8)).float().mean()), 5),
                 "saturated_frac": round(float((sc == 0xFE).float().mean()), 6),
                 "rel_l2_error": round(float(err), 5),
+                "block_rel_error_mean": round(float(blk_rel.mean()), 5),
+                "block_rel_error_median": round(float(blk_rel.median()), 5),
             }
         res[name] = entry
     return res
