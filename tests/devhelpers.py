@@ -4,7 +4,7 @@ path through the C ABI (via the binding), and compare with the oracle."""
 import numpy as np
 
 import fp4_block_scaled_amax_amd as lib
-from oracle import formats, gemm, quantize, tensor_scale
+from oracle import gemm, quantize, tensor_scale
 
 
 def dev_bf16(bits):

@@ -18,7 +18,7 @@ import fp4_block_scaled_amax_amd as lib
 from oracle import formats, quantize
 from workloads import config, random_bf16, sr_seed, STALE_FACTORS
 
-from devhelpers import (assert_entries_close, assert_gemm_close, assert_quant_equal, dev_bf16, dev_scalar,
+from devhelpers import (assert_gemm_close, assert_quant_equal, dev_bf16, dev_scalar,
                         fresh_ts, gpu_quantize, host, oracle_operand, sample_rows)
 
 pytestmark = pytest.mark.gpu

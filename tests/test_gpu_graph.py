@@ -5,7 +5,6 @@ graph and replayed several times, with eager work and synchronizations
 between the replays.  Every replay must reproduce the eager step bit for bit
 (no call records a memset node: scalars are cleared by kernels)."""
 
-import numpy as np
 import pytest
 
 import fp4_block_scaled_amax_amd as lib
