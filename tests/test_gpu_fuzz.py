@@ -4,17 +4,21 @@ here -- ragged and strided inputs, NaN / Inf / signed-zero elements and
 all-zero blocks, tensor scales off the fresh value by non-power-of-two
 factors and special ones (0, Inf, NaN, negative, 1e-45, 3e38), both
 roundings with 64-bit seeds and 32-bit offsets, every output combination,
-the amax by-product, and GEMMs over random codes with 0x00 / 0xFF scales,
-negative tensor scales and K tails.  Every output is compared with the
-oracle: codes and scale bytes bit for bit, the amax exactly, GEMM entries
-within 1e-5 |tsA tsB| sum|a b| with the same NaN pattern.
+the amax by-product, current-tensor scaling with random max_safe, GEMMs
+over random codes with 0x00 / 0xFF scales, negative tensor scales and K
+tails, and the quantizing GEMM epilogue on exact-sum operands.  Every output
+is compared with the oracle: codes and scale bytes bit for bit, the amax and
+tensor scale exactly, GEMM entries within 1e-5 |tsA tsB| sum|a b| with the
+same NaN pattern, the epilogue's bf16 output bit for bit with the oracle's
+rounding of the exact C.
 """
 
 import numpy as np
 import pytest
 
 import fp4_block_scaled_amax_amd as lib
-from oracle import formats, mxfp4, quantize, quantize2d
+from oracle import formats, mxfp4, quantize, quantize2d, tensor_scale
+from oracle import gemm as ogemm
 
 from devhelpers import assert_gemm_close, dev_scalar, host
 from workloads import random_bf16
@@ -180,3 +184,83 @@ def test_gemm_mxfp4_random_case(cuda_device, case):
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert np.all(np.abs(got - ref)[ok] <= 1e-5 * bound[ok])
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_current_scaling_random_case(cuda_device, case):
+    rng = np.random.default_rng(10_000 + case)
+    want_row, want_col = [(True, True), (True, False), (False, True)][int(rng.integers(3))]
+    rows = 16 * int(rng.integers(1, 26)) if want_col else int(rng.integers(1, 420))
+    cols, pad = 16 * int(rng.integers(1, 42)), 8 * int(rng.integers(0, 4))
+    kind, bits = _input(rng, rows, cols)
+    if rng.random() < 0.1:
+        bits[:] = 0
+    rounding = lib.SR if rng.random() < 0.5 else lib.RNE
+    seed, offset = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**32))
+    max_safe = np.float32(7168.0 if rng.random() < 0.5 else rng.uniform(1.0, 114688.0))
+    ts_prev = np.float32(2.0 ** rng.uniform(-20, 4))
+    desc = f"case {case}: {rows}x{cols} ld+{pad} {kind} max_safe={max_safe!r} {'SR' if rounding else 'RNE'}"
+    amax_ref = quantize.tensor_amax(bits)
+    _, ts_ref = tensor_scale.update_tensor_scale(amax_ref, ts_prev, 0, 1, max_safe)
+    x = _device_strided(bits, pad)
+    ts_dev, amax_dev = dev_scalar(ts_prev), dev_scalar(123.0)
+    qr = lib.empty_quantized(rows, cols, ts_dev) if want_row else None
+    qc = lib.empty_quantized(cols, rows, ts_dev) if want_col else None
+    lib.quantize_current_scaling(x, ts_dev, amax_dev, rounding, seed, offset, row=qr, col=qc, max_safe=float(max_safe))
+    _check_amax(host(amax_dev)[0], bits)
+    assert host(ts_dev)[0].tobytes() == ts_ref.tobytes(), f"{desc}: tensor scale"
+    for q, o in ((qr, 0), (qc, 1)):
+        if q is not None:
+            oc, os_ = quantize.quantize_blockscale(bits, ts_ref, rounding, seed, offset, o)
+            _check(q, oc, os_, f"{desc}, orientation {o}")
+
+
+EXACT_CODES = np.array([0, 1, 2, 8, 9, 10], dtype=np.uint8)  # 0, 0.5, 1 and their negatives
+
+
+def _exact_operand(rng, rows, k, ts):
+    """Payload magnitudes <= 1, scales in [1, 1.875] and a power-of-two
+    tensor scale: every fp32 partial sum of the GEMM is exact (K <= 4112)."""
+    import torch
+
+    nib = rng.choice(EXACT_CODES, size=(rows, k))
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(0x78, 0x80, size=(rows, k // 16), dtype=np.uint8)
+    q = lib.Quantized(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), dev_scalar(ts))
+    return q, codes, scales
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_quantizing_epilogue_random_case(cuda_device, case):
+    import torch
+
+    rng = np.random.default_rng(11_000 + case)
+    M, N, K = 16 * int(rng.integers(1, 40)), 16 * int(rng.integers(1, 40)), 16 * int(rng.integers(0, 70))
+    ta = np.float32((-1.0 if rng.random() < 0.3 else 1.0) * 2.0 ** int(rng.integers(-10, 5)))
+    tb = np.float32(2.0 ** int(rng.integers(-10, 5)))
+    a, ac, asc = _exact_operand(rng, M, K, ta)
+    b, bc, bsc = _exact_operand(rng, N, K, tb)
+    ref, _ = ogemm.gemm_nt(ac, asc, ta, bc, bsc, tb)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref), "operands do not give exact sums"
+    # An exact zero sum is +0 in the fp32 accumulators; the epilogue's
+    # products (acc * 256 tsA) * tsB give it the sign of tsA * tsB.
+    ref = np.where(ref == 0.0, np.copysign(0.0, float(ta) * float(tb)), ref)
+    ybits = formats.f32_to_bf16_rne(ref.astype(np.float32))
+    out_ts = _tensor_scale(rng, ybits)
+    rounding = lib.SR if rng.random() < 0.5 else lib.RNE
+    seed, offset = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**32))
+    want_row, want_col = [(True, True), (True, False), (False, True)][int(rng.integers(3))]
+    desc = f"case {case}: {M}x{N}x{K} out_ts={out_ts!r} {'SR' if rounding else 'RNE'} row={want_row} col={want_col}"
+    ts_dev = dev_scalar(out_ts)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    amax = dev_scalar(0.0)
+    qr = lib.empty_quantized(M, N, ts_dev) if want_row else None
+    qc = lib.empty_quantized(N, M, ts_dev) if want_col else None
+    lib.gemm_nt_bf16_quantized(a, b, y, ts_dev, rounding, seed, offset, row=qr, col=qc, amax=amax)
+    got = host(y.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got, ybits), f"{desc}: bf16 output"
+    _check_amax(host(amax)[0], ybits)
+    for q, o in ((qr, 0), (qc, 1)):
+        if q is not None:
+            oc, os_ = quantize.quantize_blockscale(ybits, out_ts, rounding, seed, offset, o)
+            _check(q, oc, os_, f"{desc}, orientation {o}")
