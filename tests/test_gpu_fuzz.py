@@ -264,3 +264,33 @@ def test_quantizing_epilogue_random_case(cuda_device, case):
         if q is not None:
             oc, os_ = quantize.quantize_blockscale(ybits, out_ts, rounding, seed, offset, o)
             _check(q, oc, os_, f"{desc}, orientation {o}")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_exact_sum_outputs_random_case(cuda_device, case):
+    """fp32 and bf16 (+ amax) outputs on exact-sum operands, ragged M and N,
+    tensor scales of either sign: bit for bit, zero signs included (R20)."""
+    import torch
+
+    rng = np.random.default_rng(12_000 + case)
+    M, N, K = int(rng.integers(1, 620)), int(rng.integers(1, 620)), 16 * int(rng.integers(0, 70))
+    ta = np.float32((-1.0 if rng.random() < 0.4 else 1.0) * 2.0 ** int(rng.integers(-10, 5)))
+    tb = np.float32((-1.0 if rng.random() < 0.4 else 1.0) * 2.0 ** int(rng.integers(-10, 5)))
+    a, ac, asc = _exact_operand(rng, M, K, ta)
+    b, bc, bsc = _exact_operand(rng, N, K, tb)
+    ref, _ = ogemm.gemm_nt(ac, asc, ta, bc, bsc, tb)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref), "operands do not give exact sums"
+    ref = np.where(ref == 0.0, np.copysign(0.0, float(ta) * float(tb)), ref).astype(np.float32)
+    desc = f"case {case}: {M}x{N}x{K} ta={ta!r} tb={tb!r}"
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    lib.gemm_nt(a, b, c)
+    bad = np.argwhere(host(c).view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"{desc}: fp32 output differs at {bad[:4].tolist()}"
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    amax = dev_scalar(0.0)
+    lib.gemm_nt_bf16(a, b, y, amax=amax)
+    ybits = formats.f32_to_bf16_rne(ref)
+    got = host(y.view(torch.int16)).view(np.uint16)
+    bad = np.argwhere(got != ybits)
+    assert bad.size == 0, f"{desc}: bf16 output differs at {bad[:4].tolist()}"
+    _check_amax(host(amax)[0], ybits)
