@@ -294,3 +294,43 @@ def test_exact_sum_outputs_random_case(cuda_device, case):
     bad = np.argwhere(got != ybits)
     assert bad.size == 0, f"{desc}: bf16 output differs at {bad[:4].tolist()}"
     _check_amax(host(amax)[0], ybits)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_gemm_multi_tile_random_case(cuda_device, case):
+    """Random sizes past the 8-tile threshold of the XCD-remapped tile order
+    (up to 13 x 13 tiles, ragged tile-row groups and edges): whole output."""
+    import torch
+
+    rng = np.random.default_rng(13_000 + case)
+    M, N = int(rng.integers(257, 3300)), int(rng.integers(257, 3300))
+    K = 16 * int(rng.integers(1, 40))
+    ac, asc = _random_operand(rng, M, K, 16)
+    bc, bsc = _random_operand(rng, N, K, 16)
+    ta, tb = _random_ts(rng), _random_ts(rng)
+    a = lib.Quantized(torch.from_numpy(ac).cuda(), torch.from_numpy(asc).cuda(), dev_scalar(ta))
+    b = lib.Quantized(torch.from_numpy(bc).cuda(), torch.from_numpy(bsc).cuda(), dev_scalar(tb))
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    lib.gemm_nt(a, b, c)
+    assert_gemm_close(host(c), ac, asc, ta, bc, bsc, tb)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_quantize_multi_tile_random_case(cuda_device, case):
+    """Random sizes of many tiles (the quantizer's XCD-grouped band order),
+    both outputs, strided input."""
+    rng = np.random.default_rng(14_000 + case)
+    rows, cols = 16 * int(rng.integers(20, 130)), 16 * int(rng.integers(20, 260))
+    pad = 8 * int(rng.integers(0, 4))
+    kind, bits = _input(rng, rows, cols)
+    ts = _tensor_scale(rng, bits)
+    rounding = lib.SR if rng.random() < 0.5 else lib.RNE
+    seed, offset = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**32))
+    desc = f"case {case}: {rows}x{cols} ld+{pad} {kind} ts={ts!r} {'SR' if rounding else 'RNE'}"
+    x = _device_strided(bits, pad)
+    ts_dev = dev_scalar(ts)
+    qr, qc = lib.empty_quantized(rows, cols, ts_dev), lib.empty_quantized(cols, rows, ts_dev)
+    lib.quantize_blockscale(x, ts_dev, rounding, seed, offset, row=qr, col=qc)
+    for q, o in ((qr, 0), (qc, 1)):
+        oc, os_ = quantize.quantize_blockscale(bits, ts, rounding, seed, offset, o)
+        _check(q, oc, os_, f"{desc}, orientation {o}")
