@@ -60,8 +60,8 @@ def _quantize_rows(xo, ts, rounding, seed, offset, orientation, out_cols, row_id
     amax_b = np.max(np.abs(blocks), axis=2)  # float32, NaN propagates
 
     # 4. raw block scale
-    K = np.float32(np.float32(6.0) * ts)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        K = np.float32(np.float32(6.0) * ts)  # +Inf for ts above fp32 max / 6
         s_raw = (amax_b / K).astype(np.float32)
 
     # 5. UE5M3 code and value
