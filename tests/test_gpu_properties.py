@@ -16,7 +16,9 @@ benchmark times is checked against another launch:
 - GEMM: doubling tsA doubles C exactly (the epilogue is (acc * 256 tsA) *
   tsB); reversing the order of A's (or B's) 32-row groups, which keeps every
   row's place inside its 32 x 32 MFMA block but moves it to other tiles and
-  XCDs, permutes C's rows (columns) the same way, bit for bit;
+  XCDs, permutes C's rows (columns) the same way, bit for bit -- for the fp32
+  output, the bf16 + amax output, the quantizing epilogue (RNE, both
+  orientations) and the native MXFP4 GEMM;
 - 2-D (16 x 16 tile) scales: each element is rounded once, so the transposed
   codes are the row-wise codes transposed and both scale outputs repeat the
   tile scale (both roundings).
@@ -188,3 +190,77 @@ def test_2d_transposed_output_is_the_transpose_whole_output(c4, rounding):
     tiles = qr.scales[::16]                                           # [R/16][C/16]
     assert same(qr.scales, tiles.repeat_interleave(16, dim=0))
     assert same(qc.scales, tiles.t().contiguous().repeat_interleave(16, dim=0))
+
+
+@pytest.mark.parametrize("operand", ["A", "B"])
+def test_gemm_bf16_tile_permutation_whole_output(up_operands, operand):
+    """The bf16 + amax epilogue at the up projection's fprop shape (2048
+    tiles): reversing A's (B's) 32-row groups permutes the output's rows
+    (columns) bit for bit and keeps the amax."""
+    import torch
+
+    a, b = up_operands
+    M, N = a.rows, b.rows
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yp = torch.empty_like(y)
+    am, amp = dev_scalar(0.0), dev_scalar(0.0)
+    lib.gemm_nt_bf16(a, b, y, amax=am)
+    if operand == "A":
+        idx = _reverse_groups(M)
+        lib.gemm_nt_bf16(lib.Quantized(a.codes[idx].contiguous(), a.scales[idx].contiguous(), a.ts), b, yp, amax=amp)
+        assert same(yp.view(torch.int16), y.view(torch.int16)[idx])
+    else:
+        idx = _reverse_groups(N)
+        lib.gemm_nt_bf16(a, lib.Quantized(b.codes[idx].contiguous(), b.scales[idx].contiguous(), b.ts), yp, amax=amp)
+        assert same(yp.view(torch.int16), y.view(torch.int16)[:, idx])
+    assert same(am, amp)
+
+
+def test_quantizing_epilogue_tile_permutation_whole_output(up_operands):
+    """The quantizing epilogue (RNE, both orientations) at the same shape:
+    reversing A's 32-row groups permutes the bf16 output's rows, the
+    row-wise codes' and scales' rows, and in the transposed output each
+    row's 16-byte code groups and 2-byte scale groups (a 32-row group is 16
+    code bytes and 2 scale bytes there); the amax is kept."""
+    import torch
+
+    a, b = up_operands
+    M, N = a.rows, b.rows
+    ts = dev_scalar(2.0 ** -10)
+    idx = _reverse_groups(M)
+    ap = lib.Quantized(a.codes[idx].contiguous(), a.scales[idx].contiguous(), a.ts)
+    outs = []
+    for opa in (a, ap):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        qr, qc = lib.empty_quantized(M, N, ts), lib.empty_quantized(N, M, ts)
+        am = dev_scalar(0.0)
+        lib.gemm_nt_bf16_quantized(opa, b, y, ts, lib.RNE, row=qr, col=qc, amax=am)
+        outs.append((y, qr, qc, am))
+    (y, qr, qc, am), (yp, qrp, qcp, amp) = outs
+    g = M // 32
+    assert same(yp.view(torch.int16), y.view(torch.int16)[idx])
+    assert same(qrp.codes, qr.codes[idx]) and same(qrp.scales, qr.scales[idx])
+    assert same(qcp.codes.view(N, g, 16), qc.codes.view(N, g, 16).flip(1))
+    assert same(qcp.scales.view(N, g, 2), qc.scales.view(N, g, 2).flip(1))
+    assert same(am, amp)
+
+
+def test_mxfp4_tile_permutation_whole_output(cuda_device):
+    """The native MXFP4 GEMM at the benchmark's shape (8192 x 4096 x 16384,
+    512 tiles): reversing A's 32-row groups permutes C's rows bit for bit."""
+    import torch
+
+    M, N, K = 8192, 4096, 16384
+    g = torch.Generator(device="cuda").manual_seed(29)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    bc = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    asc = torch.randint(110, 140, (M, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    bsc = torch.randint(110, 140, (N, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    one = dev_scalar(1.0)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    cp = torch.empty_like(c)
+    lib.gemm_nt_mxfp4(ac, asc, one, bc, bsc, one, c)
+    idx = _reverse_groups(M)
+    lib.gemm_nt_mxfp4(ac[idx].contiguous(), asc[idx].contiguous(), one, bc, bsc, one, cp)
+    assert same(cp, c[idx])
+    assert bool(torch.isfinite(c).all())
