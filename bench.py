@@ -63,9 +63,9 @@ CPU_QUANT_ROWS = 3072  # output rows per orientation of dY_up in the oracle's ti
 
 def parse():
     p = argparse.ArgumentParser()
-    p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--gpus", type=int, default=1, help="GPUs to run on (one GPU only; more exits with a message)")
+    p.add_argument("--steps", type=int, default=10, help="timed FFN-pair training steps")
+    p.add_argument("--warmup", type=int, default=3, help="untimed steps before the timed ones")
     p.add_argument("--period", type=int, default=1, help="tensor-scale refresh period")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantize-only", action="store_true",
