@@ -1,5 +1,6 @@
 """Every call launches on the stream it is given (the C ABI's `stream`
-argument; the binding passes torch's current stream when none is given).
+argument; the binding passes torch's current stream when none is given),
+and calls from several host threads at once do not interfere.
 
 A side stream first spins for a bounded time (torch.cuda._sleep) and then
 copies the input into x.  A call on that stream is ordered after the copy;
@@ -143,3 +144,43 @@ def test_refresh_and_gemms_run_on_the_given_stream(inputs):
     for i, (a, b) in enumerate(zip(got, ref)):
         assert bool(torch.equal(a, b)), f"output {i} differs"
     assert float(np.abs(got[3].cpu().numpy()).max()) > 0.0
+
+
+def test_concurrent_calls_from_two_host_threads(inputs):
+    """The library keeps no state: two host threads (ctypes releases the
+    interpreter lock during each call) quantizing and running fprop on their
+    own streams at the same time get the results of serial calls."""
+    import threading
+
+    import torch
+
+    src, ts = inputs
+    R, C = src.shape
+    ref_r, ref_c, ref_a = _quantize(src, ts, lib.SR)
+    y_ref = torch.empty((R, R), dtype=torch.float32, device="cuda")
+    lib.gemm_fprop(ref_r, ref_r, y_ref)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for it in range(20):
+                    qr, qc, amax = _quantize(src, ts, lib.SR)
+                    y = torch.empty((R, R), dtype=torch.float32, device="cuda")
+                    lib.gemm_fprop(qr, qr, y)
+                    s.synchronize()
+                    ok = (torch.equal(qr.codes, ref_r.codes) and torch.equal(qc.scales, ref_c.scales)
+                          and torch.equal(amax, ref_a) and torch.equal(y, y_ref))
+                    results[(tid, it)] = bool(ok)
+        except Exception as ex:  # reported below
+            errors.append(repr(ex))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    assert not errors, errors
+    assert len(results) == 40 and all(results.values())
