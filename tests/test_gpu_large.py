@@ -109,6 +109,35 @@ def test_gemm_output_past_2_31_entries(cuda_device):
     torch.cuda.empty_cache()
 
 
+def test_mxfp4_gemm_output_past_2_31_entries(cuda_device):
+    """The native MXFP4 GEMM with an output past 2^31 entries: sampled
+    entries against the oracle, every entry written (NaN-prefilled, checked
+    finite band by band)."""
+    import torch
+    from oracle import mxfp4
+
+    M, N, K = 65536, 36864, 32
+    rng = np.random.default_rng(10)
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, size=(M, K // 32), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    bsc = rng.integers(110, 140, size=(N, K // 32), dtype=np.uint8)
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    assert c.numel() > 2**31
+    lib.gemm_nt_mxfp4(torch.from_numpy(ac).cuda(), torch.from_numpy(asc).cuda(), dev_scalar(0.5),
+                      torch.from_numpy(bc).cuda(), torch.from_numpy(bsc).cuda(), dev_scalar(0.25), c)
+    rows = np.array([0, 1, 30000, 58254, 65535, 65535, 40000, 65535])
+    cols = np.array([0, 36863, 17, 36000, 0, 36863, 12345, 36000])
+    got = host(c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()]).astype(np.float64)
+    ref, bound = mxfp4.gemm_nt_mx(ac[rows], asc[rows], 0.5, bc[cols], bsc[cols], 0.25)
+    ref, bound = np.diag(ref), np.diag(bound)
+    assert np.all(np.abs(got - ref) <= 1e-5 * bound)
+    for r in range(0, M, 8192):
+        assert bool(torch.isfinite(c[r:r + 8192]).all()), f"unwritten or non-finite entries in rows {r}.."
+    del c
+    torch.cuda.empty_cache()
+
+
 # Past 2^35 elements the stochastic-rounding call numbers (element index / 8)
 # no longer fit 32 bits: the kernels take the 64-bit counter form there.
 # x is a generator block of BR x BC tiled on the device to R35 x C35
