@@ -138,6 +138,64 @@ def test_mxfp4_gemm_output_past_2_31_entries(cuda_device):
     torch.cuda.empty_cache()
 
 
+def test_dequantize_past_2_31_elements(cuda_device):
+    """Dequantize of a 65536 x 32784 operand (past 2^31 elements): sampled
+    rows bit-exact with the oracle's decode."""
+    import torch
+    from oracle import quantize as oq
+
+    R, C = 65536, 32784
+    rng = np.random.default_rng(11)
+    codes = torch.randint(0, 256, (R, C // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.randint(0x01, 0xFF, (R, C // 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, C), dtype=torch.float32, device="cuda")
+    assert out.numel() > 2**31
+    lib.dequantize(lib.Quantized(codes, scales, dev_scalar(0.375)), out)
+    rows = np.unique(np.concatenate([[0, 1, R - 1], rng.integers(0, R, size=5)]))
+    idx = torch.from_numpy(rows).cuda()
+    want = oq.dequantize(host(codes[idx]), host(scales[idx]), np.float32(0.375))
+    assert np.array_equal(host(out[idx]).view(np.uint32), want.astype(np.float32).view(np.uint32))
+    del out, codes, scales
+    torch.cuda.empty_cache()
+
+
+def test_gemm_bf16_output_past_2_31_entries(cuda_device):
+    """The bf16 + amax epilogue with an output past 2^31 entries, on
+    exact-sum operands (payloads 0, +-0.5, +-1; scales in [1, 1.875];
+    power-of-two tensor scales): sampled entries bit-exact with the oracle's
+    rounding of the exact C, every entry written (NaN-prefilled)."""
+    import torch
+    from oracle import formats
+    from oracle import gemm as og
+
+    M, N, K = 65536, 36864, 32
+    rng = np.random.default_rng(12)
+
+    def exact(rows):
+        nib = rng.choice(np.array([0, 1, 2, 8, 9, 10], dtype=np.uint8), size=(rows, K))
+        return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8), \
+            rng.integers(0x78, 0x80, size=(rows, K // 16), dtype=np.uint8)
+
+    ac, asc = exact(M)
+    bc, bsc = exact(N)
+    a = lib.Quantized(torch.from_numpy(ac).cuda(), torch.from_numpy(asc).cuda(), dev_scalar(0.5))
+    b = lib.Quantized(torch.from_numpy(bc).cuda(), torch.from_numpy(bsc).cuda(), dev_scalar(0.25))
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert y.numel() > 2**31
+    lib.gemm_nt_bf16(a, b, y, amax=dev_scalar(0.0))
+    rows = np.array([0, 1, 30000, 58254, 65535, 65535, 40000, 65535])
+    cols = np.array([0, 36863, 17, 36000, 0, 36863, 12345, 36000])
+    ref, _ = og.gemm_nt(ac[rows], asc[rows], 0.5, bc[cols], bsc[cols], 0.25)
+    ref = np.diag(ref) + 0.0
+    want = formats.f32_to_bf16_rne(ref.astype(np.float32))
+    got = host(y.view(torch.int16)[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()]).view(np.uint16)
+    assert np.array_equal(got, want)
+    for r in range(0, M, 8192):
+        assert bool(torch.isfinite(y[r:r + 8192]).all()), f"unwritten entries in rows {r}.."
+    del y
+    torch.cuda.empty_cache()
+
+
 # Past 2^35 elements the stochastic-rounding call numbers (element index / 8)
 # no longer fit 32 bits: the kernels take the 64-bit counter form there.
 # x is a generator block of BR x BC tiled on the device to R35 x C35
