@@ -84,6 +84,39 @@ def test_quantize_2d_past_2_31_elements(big_x):
     del qr, qc
 
 
+def test_current_scaling_past_2_31_elements(big_x):
+    """Current-tensor scaling over the same 133120 x 16384 tensor with its
+    largest magnitude (-8192) planted at the very last element, past 2^31
+    elements: the amax pass finds it, the tensor scale is amax / 43008, and
+    sampled rows of both orientations (the planted element's row and column
+    among them) are bit-exact with the oracle."""
+    import torch
+
+    block, x = big_x
+    old = x[R - 1, C - 1].clone()
+    x[R - 1, C - 1] = np.int16(np.uint16(0xC600).view(np.int16))  # bf16 -8192
+    try:
+        ts, amax = dev_scalar(1.0), dev_scalar(0.0)
+        qr, qc = lib.empty_quantized(R, C, ts), lib.empty_quantized(C, R, ts)
+        lib.quantize_current_scaling(x, ts, amax, lib.RNE, row=qr, col=qc)
+        torch.cuda.synchronize()
+        assert host(amax)[0] == np.float32(8192.0)
+        ts_val = np.float32(np.float32(8192.0) / np.float32(6.0 * 7168.0))
+        assert host(ts)[0] == ts_val
+        rows_bits = block[ROWS % PERIOD].copy()
+        rows_bits[-1, C - 1] = 0xC600  # ROWS ends with R - 1
+        c, s_ = quantize.quantize_blockscale(rows_bits, ts_val, quantize.RNE)
+        assert np.array_equal(host(qr.codes[ROWS.tolist()]), c) and np.array_equal(host(qr.scales[ROWS.tolist()]), s_)
+        cols = np.tile(block[:, [0, C - 1]], (-(-R // PERIOD), 1))[:R].copy()
+        cols[R - 1, 1] = 0xC600
+        c, s_ = quantize.quantize_blockscale(cols, ts_val, quantize.RNE, orientation=1)
+        assert np.array_equal(host(qc.codes[[0, C - 1]]), c) and np.array_equal(host(qc.scales[[0, C - 1]]), s_)
+        del qr, qc
+    finally:
+        x[R - 1, C - 1] = old
+        torch.cuda.synchronize()
+
+
 def test_gemm_output_past_2_31_entries(cuda_device):
     import torch
 
