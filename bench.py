@@ -259,6 +259,10 @@ def main():
         ref = float(np.mean(ref_ms[rounding]))
         stats["stream_reference_avg_launch_ms"] = round(ref, 4)
         stats["frac_of_stream_reference"] = round(ref / stats["avg_launch_ms"], 4)
+        # what bounds it (rocprofv3 counters of these launches): round to
+        # nearest streams HBM; stochastic rounding keeps the vector ALU busy
+        # about 90 % of cycles (Philox and the SR conversion)
+        stats["bound"] = "alu" if rounding == lib.SR else "hbm"
         return stats
 
     traffic = gemm_traffic()
